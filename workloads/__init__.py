@@ -1,0 +1,10 @@
+"""Seeded synthetic inputs for the five MoE dispatch/combine workloads.
+
+This module only draws random inputs and stores them in the formats the path
+consumes (fp32, bfloat16 bit patterns, fp8 E4M3FN bit patterns with
+per-128-element fp32 block scales).  It holds none of the routing, dispatch or
+combine arithmetic, so both the CPU oracle and the HIP path can use it.
+"""
+from .gen import CONFIGS, WorkloadConfig, make_inputs, make_swiglu_weights, alternating_sort
+
+__all__ = ["CONFIGS", "WorkloadConfig", "make_inputs", "make_swiglu_weights", "alternating_sort"]
