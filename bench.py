@@ -1,0 +1,277 @@
+"""Benchmark of the MoE route -> dispatch -> combine path on one MI355X.
+
+One step = one pass of the hot path over one batch: softmax top-k routing,
+dispatch (counts, offsets, stable positions) and the row copy into the
+expert-major buffer, identity experts (y = rows), weighted combine back to
+token order.  Inputs are resident in HBM before the timed region starts.
+
+Workload (default): prefill, N=4096 tokens, D=7168 bf16, E=256 experts, top-8,
+Zipf(1.1) expert popularity, sorted dispatch.  The decode shape (N=128,
+unsorted dispatch) is timed in the same run and reported as µs/layer beside
+it.
+
+Output: one JSON line (see the repository's bench contract) with the
+whole-path GB/s of algorithmic bytes, a roofline object for the dominant
+kernel (its duration from HIP events on the launch stream) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill.json")
+KERNEL_SOURCES = {              # kernel -> source file whose hash must match the counters
+    "scatter": "combine_moe_route_topk_amd/csrc/dispatch.hip",
+    "combine": "combine_moe_route_topk_amd/csrc/combine.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "segment", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run only a plain device copy of known size (PMC counter calibration)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ bytes per step
+
+def algorithmic_bytes(n, d, e, k, g, elem):
+    nk = n * k
+    route = n * e * 4 + 2 * nk * 4
+    maps = nk * 4 + 3 * nk * 4 + (e + (e + 1) + (g + 1)) * 4
+    scatter = n * d * elem + nk * d * elem + nk * 4
+    combine = nk * d * elem + 2 * nk * 4 + n * d * elem
+    return dict(route=route, maps=maps, scatter=scatter, combine=combine,
+                total=route + maps + scatter + combine)
+
+
+def source_sha(rel):
+    with open(os.path.join(ROOT, rel), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ GPU side
+
+class Path:
+    """Preallocated buffers and the four calls of one step."""
+
+    def __init__(self, cfg, torch, moe):
+        from workloads import make_inputs
+        self.torch, self.moe, self.cfg = torch, moe, cfg
+        dev = torch.device("cuda:0")
+        inp = make_inputs(cfg)
+        self.inputs = inp
+        n, d, e, k, g = cfg.n_tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.n_segments
+        self.logits = torch.from_numpy(inp["logits"]).to(dev)
+        if cfg.dtype == "bf16":
+            self.x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        elif cfg.dtype == "f32":
+            self.x = torch.from_numpy(inp["x"]).to(dev)
+        else:
+            raise ValueError("bench workloads carry bf16 or fp32 payloads")
+        self.idx = torch.empty((n, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((n, k), dtype=torch.float32, device=dev)
+        self.rows = torch.empty((n * k, d), dtype=self.x.dtype, device=dev)
+        self.out = torch.empty((n, d), dtype=self.x.dtype, device=dev)
+        self.ws = torch.empty(moe.moe_dispatch_workspace_bytes(n, e, k, g), dtype=torch.uint8, device=dev)
+        self.sort = cfg.sort if cfg.sort in (-1, 0, 1) else 1
+        self.res = moe.moe_dispatch(None, self.idx.zero_(), e, g, sort=self.sort, workspace=self.ws)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, ev=None):
+        moe, c = self.moe, self.cfg
+        if ev: ev[0].record(self.stream)
+        moe.moe_route_topk(self.logits, c.top_k, c.renormalize, topk_idx=self.idx, topk_w=self.w)
+        if ev: ev[1].record(self.stream)
+        moe.moe_dispatch(None, self.idx, c.n_experts, c.n_segments, sort=self.sort,
+                         sort_cutoff=c.sort_cutoff, workspace=self.ws, out=self.res)
+        if ev: ev[2].record(self.stream)
+        moe.moe_scatter_rows(self.x, self.res.dst_pos, c.top_k, rows=self.rows)
+        if ev: ev[3].record(self.stream)
+        moe.moe_combine(self.rows, self.res.dst_pos, self.w, out=self.out)
+        if ev: ev[4].record(self.stream)
+
+
+def time_path(path, steps, warmup):
+    torch = path.torch
+    for _ in range(warmup):
+        path.step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        path.step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(steps)])
+    return wall / steps * 1e3, stage.mean(axis=0) * 1e3, np.median(stage, axis=0) * 1e3
+
+
+def check_outputs(path):
+    """Spot-check the timed buffers against the oracle (a few tokens)."""
+    from oracle import codecs
+    from oracle.combine import combine_f64
+    from oracle.route import route_topk
+    torch, c = path.torch, path.cfg
+    torch.cuda.synchronize()
+    oi, _ = route_topk(path.inputs["logits"], c.top_k, c.renormalize)
+    if not np.array_equal(path.idx.cpu().numpy(), oi):
+        raise RuntimeError("routing indices of the timed run differ from the oracle")
+    toks = np.linspace(0, c.n_tokens - 1, 8).astype(int)
+    dst = path.res.dst_pos.cpu().numpy()
+    w = path.w.cpu().numpy()
+    xf = codecs.bf16_bits_to_f32(path.inputs["x"]) if c.dtype == "bf16" else path.inputs["x"]
+    rows_f = np.zeros((c.n_tokens * c.top_k, c.hidden), np.float32)
+    for t in toks:
+        for j in range(c.top_k):
+            rows_f[dst[t * c.top_k + j]] = xf[t]
+    exact = combine_f64(rows_f, dst, w, c.top_k, tokens=toks)
+    got = path.out[torch.from_numpy(toks).to(path.out.device)].float().cpu().numpy()
+    if not np.all(np.abs(got - exact) <= 2.0 ** -7 * np.abs(exact) + 1e-30):
+        raise RuntimeError("combine output of the timed run differs from the oracle")
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(cfg, n_sample, min_seconds=10.0, max_repeats=5):
+    """The oracle as it stands, on the first ``n_sample`` tokens of the same
+    workload, repeated until ~min_seconds of CPU work; median pass time."""
+    from oracle import codecs, dispatch as od
+    from oracle.combine import combine_f64
+    from oracle.route import route_topk
+    from workloads import make_inputs
+    sub = cfg.with_tokens(min(n_sample, cfg.n_tokens))
+    inp = make_inputs(sub)
+    times = []
+    while len(times) < max_repeats and (len(times) < 1 or sum(times) < min_seconds):
+        t0 = time.perf_counter()
+        idx, w = route_topk(inp["logits"], sub.top_k, sub.renormalize)
+        sorted_ = od.resolve_sorted(cfg.sort if cfg.sort in (-1, 0, 1) else 1, sub.n_tokens,
+                                    sub.sort_cutoff)
+        res = od.dispatch(idx, sub.n_experts, sub.n_segments, sorted_, x=inp["x"])
+        y = codecs.bf16_bits_to_f32(res["rows"]) if sub.dtype == "bf16" else res["rows"]
+        out = combine_f64(y, res["dst_pos"], w, sub.top_k)
+        if sub.dtype == "bf16":
+            codecs.f64_to_bf16_bits(out)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    b = algorithmic_bytes(sub.n_tokens, sub.hidden, sub.n_experts, sub.top_k, sub.n_segments,
+                          sub.elem_bytes)["total"]
+    return dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{sub.n_tokens} of {cfg.n_tokens} tokens of the same workload; median of "
+                       f"{len(times)} passes of route+dispatch+combine ({sum(times):.1f} s total, "
+                       "numpy, single-threaded)",
+                seconds_per_pass=round(dt, 3))
+
+
+# ------------------------------------------------------------------ main
+
+def calib_copy(torch):
+    """A plain device copy of 1 GiB, for scaling FETCH_SIZE / WRITE_SIZE."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build runs the single-GPU share of the path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calib_copy:
+        calib_copy(torch)
+        return
+    import combine_moe_route_topk_amd as moe
+    from workloads import CONFIGS
+
+    cfg = CONFIGS[args.workload]
+    path = Path(cfg, torch, moe)
+    ms, stage_mean_us, stage_med_us = time_path(path, args.steps, args.warmup)
+    check_outputs(path)
+    n, d, e, k, g = cfg.n_tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.n_segments
+    b = algorithmic_bytes(n, d, e, k, g, cfg.elem_bytes)
+    value = b["total"] / (ms * 1e-3) / 1e9
+
+    names = ["route", "maps", "scatter", "combine"]
+    dom = "scatter" if stage_mean_us[2] >= stage_mean_us[3] else "combine"
+    di = names.index(dom)
+    achieved = b[dom] / (stage_mean_us[di] * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        ent = tr.get(dom)
+        if ent and ent.get("source_sha") == source_sha(KERNEL_SOURCES[dom]) and tr.get("workload") == args.workload:
+            traffic = ent["hbm_bytes_per_launch"]
+    roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    algorithmic_bytes=b[dom], avg_us=round(float(stage_mean_us[di]), 2))
+
+    rec = {
+        "metric": "dispatch+combine µs/layer and HBM GB/s (% peak) at 128 and 4096 tokens",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.note}", "n_tokens": n, "hidden": d,
+                   "n_experts": e, "top_k": k, "n_segments": g,
+                   "sort": "sorted" if path.res.sorted else "unsorted", "experts": "identity",
+                   "bytes_per_step": b["total"]},
+        "us_per_layer": round(ms * 1e3, 2),
+        "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "stages_us": {nm: round(float(v), 2) for nm, v in zip(names, stage_mean_us)},
+        "roofline": roofline,
+    }
+    if not args.no_decode and args.workload == "prefill":
+        dcfg = CONFIGS["decode"]
+        dpath = Path(dcfg, torch, moe)
+        dms, dst_us, _ = time_path(dpath, max(args.steps, 200), args.warmup)
+        check_outputs(dpath)
+        db = algorithmic_bytes(dcfg.n_tokens, dcfg.hidden, dcfg.n_experts, dcfg.top_k,
+                               dcfg.n_segments, dcfg.elem_bytes)
+        rec["decode"] = {"workload": f"decode: {dcfg.note}", "us_per_layer": round(dms * 1e3, 2),
+                         "GB_per_s": round(db["total"] / (dms * 1e-3) / 1e9, 1),
+                         "cache": "hot (33 MB of buffers stay in the 256 MB last-level cache)",
+                         "stages_us": {nm: round(float(v), 2) for nm, v in zip(names, dst_us)}}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,17 @@
+"""MI355X (gfx950) MoE routing, dispatch and combine.
+
+The compute lives in the HIP library ``libmoe_dc.so`` (C ABI in
+``include/moe_dc.h``); this package is its PyTorch binding.  Importing it
+without the built library raises ImportError -- there is no CPU fallback.
+"""
+from .api import (DispatchResult, MoeError, moe_abi_version, moe_combine, moe_dequant_rows,
+                  moe_dispatch, moe_dispatch_workspace_bytes, moe_gather_rows, moe_grouped_swiglu,
+                  moe_grouped_swiglu_workspace_bytes, moe_resolve_sorted, moe_route_topk,
+                  moe_scatter_rows)
+from ._lib import LIB_PATH, MOE_SORT_AUTO, MOE_SORT_OFF, MOE_SORT_ON
+
+__all__ = ["DispatchResult", "MoeError", "moe_abi_version", "moe_combine", "moe_dequant_rows",
+           "moe_dispatch", "moe_dispatch_workspace_bytes", "moe_gather_rows", "moe_grouped_swiglu",
+           "moe_grouped_swiglu_workspace_bytes", "moe_resolve_sorted", "moe_route_topk",
+           "moe_scatter_rows",
+           "LIB_PATH", "MOE_SORT_AUTO", "MOE_SORT_OFF", "MOE_SORT_ON"]

@@ -1,0 +1,236 @@
+"""Thin PyTorch binding of libmoe_dc: same names as the C ABI.
+
+Each function checks that its tensors are contiguous device tensors of the
+expected dtype, allocates any output that was not passed in (torch owns all
+device memory), and calls the C function on the current HIP stream.  Every
+step of the computation runs in the library's HIP kernels; nothing here
+computes.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from ._lib import (MOE_BF16, MOE_F32, MOE_F8E4M3, MOE_SORT_AUTO, MoeError, check, lib)
+
+__all__ = ["moe_route_topk", "moe_resolve_sorted", "moe_dispatch_workspace_bytes", "moe_dispatch",
+           "moe_combine", "moe_dequant_rows", "moe_scatter_rows", "moe_gather_rows", "moe_grouped_swiglu_workspace_bytes",
+           "moe_grouped_swiglu", "moe_abi_version", "DispatchResult", "MoeError"]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+_PAYLOAD = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.uint8: MOE_F8E4M3,
+            torch.float8_e4m3fn: MOE_F8E4M3}
+_FLOAT_IO = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+
+def moe_abi_version() -> int:
+    return lib.moe_abi_version()
+
+
+def moe_route_topk(logits: torch.Tensor, k: int, renormalize: bool = True,
+                   topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                   stream=None):
+    """logits [N, E] float32 -> (topk_idx [N, k] int32, topk_w [N, k] float32)."""
+    _need(logits, "logits", (torch.float32,))
+    n, e = logits.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((n, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((n, k), dtype=torch.float32, device=logits.device)
+    _need(topk_idx, "topk_idx", (torch.int32,), logits.device)
+    _need(topk_w, "topk_w", (torch.float32,), logits.device)
+    if topk_idx.numel() != n * k or topk_w.numel() != n * k:
+        raise ValueError("topk_idx / topk_w must hold N*k elements")
+    check("moe_route_topk", lib.moe_route_topk(_ptr(logits), n, e, k, int(bool(renormalize)),
+                                               _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_resolve_sorted(sort: int, n_tokens: int, sort_cutoff: int) -> bool:
+    out = ctypes.c_int32(-1)
+    check("moe_resolve_sorted", lib.moe_resolve_sorted(sort, n_tokens, sort_cutoff, ctypes.byref(out)))
+    return bool(out.value)
+
+
+def moe_dispatch_workspace_bytes(n_tokens: int, n_experts: int, k: int, n_segments: int = 1) -> int:
+    return int(lib.moe_dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments))
+
+
+@dataclass
+class DispatchResult:
+    sorted: bool
+    expert_counts: torch.Tensor
+    expert_offsets: torch.Tensor
+    segment_offsets: torch.Tensor
+    src_pair: torch.Tensor
+    dst_pos: torch.Tensor
+    row_expert: Optional[torch.Tensor]
+    rows: Optional[torch.Tensor]
+    row_scales: Optional[torch.Tensor]
+
+
+def moe_dispatch(x: Optional[torch.Tensor], topk_idx: torch.Tensor, n_experts: int,
+                 n_segments: int = 1, sort: int = MOE_SORT_AUTO, sort_cutoff: int = 256,
+                 x_scales: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 out: Optional[DispatchResult] = None, want_row_expert: bool = True,
+                 stream=None) -> DispatchResult:
+    """Stable expert-major (sorted) or segment-major (unsorted) dispatch.
+
+    x [N, D] float32 / bfloat16 / uint8-or-float8_e4m3fn (then x_scales
+    [N, D/128] float32), or None to compute the maps only.  ``out`` may carry
+    preallocated outputs (reused in place)."""
+    _need(topk_idx, "topk_idx", (torch.int32,))
+    dev = topk_idx.device
+    n, k = topk_idx.shape
+    nk = n * k
+    if x is not None:
+        _need(x, "x", tuple(_PAYLOAD), dev)
+        if x.shape[0] != n:
+            raise ValueError("x and topk_idx disagree on N")
+        dtype, hidden = _PAYLOAD[x.dtype], x.shape[1]
+    else:
+        dtype, hidden = MOE_BF16, 1
+    if x_scales is not None:
+        _need(x_scales, "x_scales", (torch.float32,), dev)
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        rows = None if x is None else torch.empty((nk, hidden), dtype=x.dtype, device=dev)
+        rs = None if x_scales is None else torch.empty((nk, x_scales.shape[1]), dtype=torch.float32, device=dev)
+        out = DispatchResult(False, torch.empty(n_experts, **i32), torch.empty(n_experts + 1, **i32),
+                             torch.empty(n_segments + 1, **i32), torch.empty(nk, **i32),
+                             torch.empty(nk, **i32),
+                             torch.empty(nk, **i32) if want_row_expert else None, rows, rs)
+    if workspace is None:
+        wsb = moe_dispatch_workspace_bytes(n, n_experts, k, n_segments)
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), dev)
+    used = ctypes.c_int32(-1)
+    check("moe_dispatch", lib.moe_dispatch(
+        _ptr(x), _ptr(x_scales), dtype, n, hidden, _ptr(topk_idx), n_experts, k, n_segments, sort,
+        sort_cutoff, ctypes.byref(used), _ptr(out.rows), _ptr(out.row_scales),
+        _ptr(out.expert_counts), _ptr(out.expert_offsets), _ptr(out.segment_offsets),
+        _ptr(out.src_pair), _ptr(out.dst_pos), _ptr(out.row_expert), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    out.sorted = bool(used.value)
+    return out
+
+
+def moe_scatter_rows(x: torch.Tensor, dst_pos: torch.Tensor, k: int,
+                     rows: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rows[dst_pos[t*k+j]] = x[t] (bytes copied unchanged).  x [N, ...] contiguous."""
+    _need(x, "x", None)
+    _need(dst_pos, "dst_pos", (torch.int32,), x.device)
+    n = x.shape[0]
+    row_bytes = x[0].numel() * x.element_size() if n else max(1, x.element_size())
+    if rows is None:
+        rows = torch.empty((n * k,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+    _need(rows, "rows", (x.dtype,), x.device)
+    if dst_pos.numel() != n * k or rows.shape[0] != n * k:
+        raise ValueError("dst_pos and rows must hold N*k entries")
+    check("moe_scatter_rows", lib.moe_scatter_rows(_ptr(x), n, row_bytes, k, _ptr(dst_pos),
+                                                   _ptr(rows), _stream(stream)))
+    return rows
+
+
+def moe_gather_rows(x: torch.Tensor, src_pair: torch.Tensor, k: int,
+                    rows: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rows[p] = x[src_pair[p] // k] (bytes copied unchanged)."""
+    _need(x, "x", None)
+    _need(src_pair, "src_pair", (torch.int32,), x.device)
+    n = x.shape[0]
+    n_rows = src_pair.numel()
+    row_bytes = x[0].numel() * x.element_size() if n else max(1, x.element_size())
+    if rows is None:
+        rows = torch.empty((n_rows,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+    _need(rows, "rows", (x.dtype,), x.device)
+    check("moe_gather_rows", lib.moe_gather_rows(_ptr(x), n, row_bytes, k, _ptr(src_pair), n_rows,
+                                                 _ptr(rows), _stream(stream)))
+    return rows
+
+
+def moe_combine(y: torch.Tensor, dst_pos: torch.Tensor, topk_w: torch.Tensor,
+                out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """y [N*k, D] float32/bfloat16, dst_pos [N*k] int32, topk_w [N, k] float32 -> out [N, D]."""
+    _need(y, "y", tuple(_FLOAT_IO))
+    dev = y.device
+    _need(dst_pos, "dst_pos", (torch.int32,), dev)
+    _need(topk_w, "topk_w", (torch.float32,), dev)
+    n, k = topk_w.shape
+    hidden = y.shape[1]
+    if dst_pos.numel() != n * k or y.shape[0] != n * k:
+        raise ValueError("y / dst_pos must hold N*k rows")
+    if out is None:
+        out = torch.empty((n, hidden), dtype=out_dtype or y.dtype, device=dev)
+    _need(out, "out", tuple(_FLOAT_IO), dev)
+    check("moe_combine", lib.moe_combine(_ptr(y), _FLOAT_IO[y.dtype], n, hidden, k, _ptr(dst_pos),
+                                         _ptr(topk_w), _ptr(out), _FLOAT_IO[out.dtype],
+                                         _stream(stream)))
+    return out
+
+
+def moe_dequant_rows(rows: torch.Tensor, row_scales: torch.Tensor,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp8 E4M3FN rows [R, D] (uint8 or float8_e4m3fn) + scales [R, D/128] -> bf16 [R, D]."""
+    _need(rows, "rows", (torch.uint8, torch.float8_e4m3fn))
+    _need(row_scales, "row_scales", (torch.float32,), rows.device)
+    r, d = rows.shape
+    if out is None:
+        out = torch.empty((r, d), dtype=torch.bfloat16, device=rows.device)
+    _need(out, "out", (torch.bfloat16,), rows.device)
+    check("moe_dequant_rows", lib.moe_dequant_rows(_ptr(rows), _ptr(row_scales), r, d, _ptr(out),
+                                                   _stream(stream)))
+    return out
+
+
+def moe_grouped_swiglu_workspace_bytes(n_rows: int, n_experts: int, hidden: int, ffn: int) -> int:
+    return int(lib.moe_grouped_swiglu_workspace_bytes(n_rows, n_experts, hidden, ffn))
+
+
+def moe_grouped_swiglu(rows: torch.Tensor, expert_offsets: torch.Tensor, w_gate: torch.Tensor,
+                       w_up: torch.Tensor, w_down: torch.Tensor, y: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rows [R, D] bf16 grouped by expert; w_gate/w_up [E, F, D], w_down [E, D, F] bf16."""
+    _need(rows, "rows", (torch.bfloat16,))
+    dev = rows.device
+    for name, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, name, (torch.bfloat16,), dev)
+    _need(expert_offsets, "expert_offsets", (torch.int32,), dev)
+    r, d = rows.shape
+    e, f, _ = w_gate.shape
+    if y is None:
+        y = torch.empty_like(rows)
+    _need(y, "y", (torch.bfloat16,), dev)
+    if workspace is None:
+        workspace = torch.empty(max(moe_grouped_swiglu_workspace_bytes(r, e, d, f), 256),
+                                dtype=torch.uint8, device=dev)
+    check("moe_grouped_swiglu", lib.moe_grouped_swiglu(
+        _ptr(rows), r, d, _ptr(expert_offsets), e, _ptr(w_gate), _ptr(w_up), _ptr(w_down), f,
+        _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return y

@@ -1,0 +1,280 @@
+// C ABI of libmoe_dc: argument checking, mode resolution, workspace sizing and
+// error reporting.  Every check runs on the host before any HIP call, so a
+// rejected call touches no device state.
+#include "../../include/moe_dc.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool validate_mode() {
+  const char* v = std::getenv("MOE_DC_VALIDATE");
+  return v && v[0] == '1';
+}
+
+int check_routing_sizes(const char* fn, int64_t n_tokens, int32_t n_experts, int32_t k) {
+  if (n_tokens < 0) return fail(MOE_ERR_ARG, "%s: n_tokens < 0", fn);
+  if (n_experts < 1) return fail(MOE_ERR_ARG, "%s: n_experts < 1", fn);
+  if (k < 1 || k > n_experts) return fail(MOE_ERR_ARG, "%s: need 1 <= k <= n_experts (k=%d, E=%d)", fn, k, n_experts);
+  if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "%s: n_experts > %d", fn, MOE_MAX_EXPERTS);
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "%s: k > %d", fn, MOE_MAX_TOPK);
+  if (n_tokens > 0 && n_tokens * int64_t(k) > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: n_tokens * k exceeds the int32 index range", fn);
+  return MOE_OK;
+}
+
+int resolve_sorted(int32_t sort, int64_t n_tokens, int32_t cutoff, int32_t* out) {
+  if (sort == MOE_SORT_ON) { *out = 1; return MOE_OK; }
+  if (sort == MOE_SORT_OFF) { *out = 0; return MOE_OK; }
+  if (sort != MOE_SORT_AUTO) return fail(MOE_ERR_ARG, "sort must be -1, 0 or 1 (got %d)", sort);
+  if (cutoff <= 0) { *out = 1; return MOE_OK; }
+  // (M - 1) // cutoff >= 1  <=>  M > cutoff, for M >= 1
+  *out = n_tokens > cutoff ? 1 : 0;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_DC_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_resolve_sorted(int32_t sort, int64_t n_tokens, int32_t sort_cutoff, int32_t* sorted_out) {
+  if (!sorted_out) return fail(MOE_ERR_ARG, "moe_resolve_sorted: sorted_out is null");
+  if (n_tokens < 0) return fail(MOE_ERR_ARG, "moe_resolve_sorted: n_tokens < 0");
+  const int rc = resolve_sorted(sort, n_tokens, sort_cutoff, sorted_out);
+  return rc == MOE_OK ? ok() : rc;
+}
+
+int moe_route_topk(const float* logits, int64_t n_tokens, int32_t n_experts, int32_t k,
+                   int32_t renormalize, int32_t* topk_idx, float* topk_w, void* stream) {
+  const char* fn = "moe_route_topk";
+  int rc = check_routing_sizes(fn, n_tokens, n_experts, k);
+  if (rc) return rc;
+  if (n_tokens == 0) return ok();
+  if (!logits || !topk_idx || !topk_w) return fail(MOE_ERR_ARG, "%s: null pointer argument", fn);
+  return hip_status(moe::launch_route_topk(logits, n_tokens, n_experts, k, renormalize ? 1 : 0,
+                                           topk_idx, topk_w, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t moe_dispatch_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t k,
+                                    int32_t n_segments) {
+  if (n_tokens < 0 || n_experts < 1 || n_experts > MOE_MAX_EXPERTS || k < 1 || k > n_experts ||
+      k > MOE_MAX_TOPK || n_segments < 1 || n_experts % n_segments != 0 ||
+      n_tokens * int64_t(k) > INT32_MAX)
+    return 0;
+  return moe::dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments);
+}
+
+int moe_dispatch(const void* x, const float* x_scales, int32_t dtype, int64_t n_tokens,
+                 int64_t hidden, const int32_t* topk_idx, int32_t n_experts, int32_t k,
+                 int32_t n_segments, int32_t sort, int32_t sort_cutoff, int32_t* sorted_used,
+                 void* rows, float* row_scales, int32_t* expert_counts, int32_t* expert_offsets,
+                 int32_t* segment_offsets, int32_t* src_pair, int32_t* dst_pos,
+                 int32_t* row_expert, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_dispatch";
+  int rc = check_routing_sizes(fn, n_tokens, n_experts, k);
+  if (rc) return rc;
+  if (hidden < 1) return fail(MOE_ERR_ARG, "%s: hidden < 1", fn);
+  if (n_segments < 1 || n_experts % n_segments != 0)
+    return fail(MOE_ERR_ARG, "%s: n_segments must divide n_experts (E=%d, G=%d)", fn, n_experts, n_segments);
+  int64_t elem = 0;
+  switch (dtype) {
+    case MOE_F32: elem = 4; break;
+    case MOE_BF16: elem = 2; break;
+    case MOE_F8E4M3: elem = 1; break;
+    default: return fail(MOE_ERR_ARG, "%s: unknown dtype %d", fn, dtype);
+  }
+  if ((x == nullptr) != (rows == nullptr))
+    return fail(MOE_ERR_ARG, "%s: x and rows must both be given or both be null", fn);
+  if (dtype == MOE_F8E4M3) {
+    if (hidden % 128 != 0) return fail(MOE_ERR_ARG, "%s: F8 payload needs hidden %% 128 == 0", fn);
+    if (x && (!x_scales || !row_scales))
+      return fail(MOE_ERR_ARG, "%s: F8 payload needs x_scales and row_scales", fn);
+  } else if (x_scales || row_scales) {
+    return fail(MOE_ERR_ARG, "%s: block scales are only for the F8 payload", fn);
+  }
+  if (!x && (x_scales || row_scales))
+    return fail(MOE_ERR_ARG, "%s: scales given without a payload", fn);
+  if (!expert_counts || !expert_offsets || !segment_offsets)
+    return fail(MOE_ERR_ARG, "%s: null offsets/counts output", fn);
+  if (n_tokens > 0 && (!topk_idx || !src_pair || !dst_pos))
+    return fail(MOE_ERR_ARG, "%s: null index input or map output", fn);
+  int32_t sorted = 0;
+  rc = resolve_sorted(sort, n_tokens, sort_cutoff, &sorted);
+  if (rc) return rc;
+  const size_t need = moe::dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : size_t(0));
+  if (reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
+  if (sorted_used) *sorted_used = sorted;
+
+  moe::DispatchArgs a{};
+  a.x = x;
+  a.x_scales = x_scales;
+  a.row_bytes = hidden * elem;
+  a.scale_bytes = dtype == MOE_F8E4M3 ? hidden / 128 * 4 : 0;
+  a.n_tokens = n_tokens;
+  a.topk_idx = topk_idx;
+  a.n_experts = n_experts;
+  a.k = k;
+  a.n_segments = n_segments;
+  a.sorted = sorted;
+  a.rows = rows;
+  a.row_scales = row_scales;
+  a.expert_counts = expert_counts;
+  a.expert_offsets = expert_offsets;
+  a.segment_offsets = segment_offsets;
+  a.src_pair = src_pair;
+  a.dst_pos = dst_pos;
+  a.row_expert = row_expert;
+  a.workspace = workspace;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool validate = validate_mode();
+  int32_t* status = nullptr;
+  if (validate) {
+    // the status word sits in the last 16 bytes of the workspace region
+    status = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + need - 16);
+    hipError_t e = hipMemsetAsync(status, 0, sizeof(int32_t), s);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  a.status = status;
+  rc = hip_status(moe::launch_dispatch(a, s), fn);
+  if (rc || !validate) return rc;
+  int32_t host_status = 0;
+  hipError_t e = hipMemcpyAsync(&host_status, status, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (host_status) return fail(MOE_ERR_ARG, "%s: topk_idx holds expert ids outside [0, %d)", fn, n_experts);
+  return ok();
+}
+
+int moe_scatter_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int32_t k,
+                     const int32_t* dst_pos, void* rows, void* stream) {
+  const char* fn = "moe_scatter_rows";
+  if (n_tokens < 0 || row_bytes < 1 || k < 1) return fail(MOE_ERR_ARG, "%s: need n_tokens >= 0, row_bytes >= 1, k >= 1", fn);
+  if (n_tokens * int64_t(k) > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: n_tokens * k exceeds the int32 index range", fn);
+  if (n_tokens == 0) return ok();
+  if (!x || !dst_pos || !rows) return fail(MOE_ERR_ARG, "%s: null pointer argument", fn);
+  return hip_status(moe::launch_scatter_rows(x, n_tokens, row_bytes, k, dst_pos, rows,
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int moe_gather_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int32_t k,
+                    const int32_t* src_pair, int64_t n_rows, void* rows, void* stream) {
+  const char* fn = "moe_gather_rows";
+  if (n_tokens < 0 || n_rows < 0 || row_bytes < 1 || k < 1)
+    return fail(MOE_ERR_ARG, "%s: need n_tokens, n_rows >= 0, row_bytes >= 1, k >= 1", fn);
+  if (n_tokens * int64_t(k) > INT32_MAX || n_rows > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: sizes exceed the int32 index range", fn);
+  if (n_rows == 0) return ok();
+  if (!x || !src_pair || !rows) return fail(MOE_ERR_ARG, "%s: null pointer argument", fn);
+  return hip_status(moe::launch_gather_rows(x, n_tokens, row_bytes, k, src_pair, n_rows, rows,
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int moe_combine(const void* y, int32_t y_dtype, int64_t n_tokens, int64_t hidden, int32_t k,
+                const int32_t* dst_pos, const float* topk_w, void* out, int32_t out_dtype,
+                void* stream) {
+  const char* fn = "moe_combine";
+  if (n_tokens < 0) return fail(MOE_ERR_ARG, "%s: n_tokens < 0", fn);
+  if (hidden < 1) return fail(MOE_ERR_ARG, "%s: hidden < 1", fn);
+  if (k < 1) return fail(MOE_ERR_ARG, "%s: k < 1", fn);
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "%s: k > %d", fn, MOE_MAX_TOPK);
+  if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
+    return fail(MOE_ERR_ARG, "%s: y and out must be MOE_F32 or MOE_BF16", fn);
+  if (n_tokens * int64_t(k) > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: n_tokens * k exceeds the int32 index range", fn);
+  if (n_tokens == 0) return ok();
+  if (!y || !dst_pos || !topk_w || !out) return fail(MOE_ERR_ARG, "%s: null pointer argument", fn);
+  return hip_status(moe::launch_combine(y, y_dtype == MOE_BF16, n_tokens, hidden, k, dst_pos,
+                                        topk_w, out, out_dtype == MOE_BF16,
+                                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int moe_dequant_rows(const uint8_t* rows, const float* row_scales, int64_t n_rows, int64_t hidden,
+                     uint16_t* y, void* stream) {
+  const char* fn = "moe_dequant_rows";
+  if (n_rows < 0) return fail(MOE_ERR_ARG, "%s: n_rows < 0", fn);
+  if (hidden < 1 || hidden % 128 != 0) return fail(MOE_ERR_ARG, "%s: hidden must be a positive multiple of 128", fn);
+  if (n_rows == 0) return ok();
+  if (!rows || !row_scales || !y) return fail(MOE_ERR_ARG, "%s: null pointer argument", fn);
+  if ((reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(y)) & 15)
+    return fail(MOE_ERR_ARG, "%s: rows and y must be 16-byte aligned", fn);
+  return hip_status(moe::launch_dequant_rows(rows, row_scales, n_rows, hidden, y,
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t moe_grouped_swiglu_workspace_bytes(int64_t n_rows, int32_t n_experts, int64_t hidden,
+                                          int64_t ffn) {
+  if (n_rows < 0 || n_experts < 1 || hidden < 1 || ffn < 1) return 0;
+  return moe::grouped_swiglu_workspace_bytes(n_rows, n_experts, hidden, ffn);
+}
+
+int moe_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
+                       const int32_t* expert_offsets, int32_t n_experts, const void* w_gate,
+                       const void* w_up, const void* w_down, int64_t ffn, void* y,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_grouped_swiglu";
+  if (n_rows < 0) return fail(MOE_ERR_ARG, "%s: n_rows < 0", fn);
+  if (hidden < 1 || ffn < 1 || n_experts < 1) return fail(MOE_ERR_ARG, "%s: sizes must be >= 1", fn);
+  if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "%s: n_experts > %d", fn, MOE_MAX_EXPERTS);
+  if (hidden % 64 != 0 || ffn % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: hidden and ffn must be multiples of 64", fn);
+  if (n_rows > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: n_rows exceeds the int32 range", fn);
+  if (n_rows == 0) return ok();
+  if (!rows || !expert_offsets || !w_gate || !w_up || !w_down || !y)
+    return fail(MOE_ERR_ARG, "%s: null pointer argument", fn);
+  const size_t need = moe::grouped_swiglu_workspace_bytes(n_rows, n_experts, hidden, ffn);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : size_t(0));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  return hip_status(moe::launch_grouped_swiglu(rows, n_rows, hidden, expert_offsets, n_experts,
+                                               w_gate, w_up, w_down, ffn, y, workspace,
+                                               static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,512 @@
+// Dispatch: per-expert counts, prefix sums, stable position assignment and the
+// row copy into expert-major (or segment-major) buffers.
+//
+// Semantics ("backends/mlx: runtime MoE expert-sort for decode (issue
+// #20554)", author's follow-up "Handler fixes" and CI write-up): the routed
+// pairs q = t*k + j are the flattened [N, top_k] expert ids; the sorted layout
+// is a stable sort of those keys (token = order / top_k), the unsorted layout
+// with one segment is the identity (x repeated top_k times).  Segments
+// ("One-Sided Expert-Parallel All-to-All ... over NVLink", abstract:
+// rank-major blocks) bucket pairs by expert group instead of by expert.
+//
+// A stable counting sort without global atomics, so positions are
+// deterministic:
+//   count  -- each chunk of C pairs builds its expert histogram in LDS;
+//   scan   -- one workgroup turns the [P, E] histograms into expert offsets,
+//             segment offsets and per-(chunk, bucket) starting positions in
+//             (bucket-major, chunk-minor) order;
+//   rank   -- each chunk recounts per wave, then each wave walks its pairs in
+//             order, 64 at a time: ballots over the key bits give every lane
+//             the set of lanes with the same bucket, so its rank among
+//             earlier equal keys is a popcount (wave multisplit, after
+//             Ashkiani et al., "GPU Multisplit", PPoPP 2016);
+//   copy   -- scatter form: one wave reads a slice of token t's row once and
+//             writes it to the k destination rows dst_pos[t*k + j].
+// Small problems (NK <= 16384, at most 256 buckets) run count, scan and rank
+// in one workgroup.  Nothing is read back to the host: NK rows is always the
+// output size.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+constexpr int64_t kSmallMaxPairs = 16384;
+constexpr int kSmallMaxBuckets = 256;
+
+__device__ __forceinline__ int bucket_of(int e, int sorted, int per_segment) {
+  return sorted ? e : e / per_segment;
+}
+
+// Exclusive scan of one int per thread over a workgroup of up to 1024
+// threads; returns the exclusive prefix and writes the total to *total.
+__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) s_wave[w] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < nw; ++i) {
+      const int c = s_wave[i];
+      s_wave[i] = run;
+      run += c;
+    }
+    s_wave[nw] = run;
+  }
+  __syncthreads();
+  const int excl = s_wave[w] + incl - v;
+  *total = s_wave[nw];
+  return excl;
+}
+
+// Peer mask of this lane: active lanes whose key equals this lane's key.
+__device__ __forceinline__ uint64_t peer_mask(int key, bool active, int nbits) {
+  uint64_t peers = ballot(active);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool b = (key >> bit) & 1;
+    const uint64_t m = ballot(b);
+    peers &= b ? m : ~m;
+  }
+  return peers;
+}
+
+// Walk pairs [s0, s1) in order, 64 at a time, assigning positions from the
+// per-bucket running counters run[] (LDS, private to this wave).
+__device__ __forceinline__ void ordered_walk(const int32_t* __restrict__ idx, int64_t s0,
+                                             int64_t s1, int n_experts, int sorted,
+                                             int per_segment, int nbits, int* run,
+                                             int32_t* __restrict__ dst_pos,
+                                             int32_t* __restrict__ src_pair,
+                                             int32_t* __restrict__ row_expert) {
+  const int lane = lane_id();
+  for (int64_t qb = s0; qb < s1; qb += kWave) {
+    const int64_t q = qb + lane;
+    const bool in = q < s1;
+    const int e = in ? idx[q] : -1;
+    const bool ok = in && unsigned(e) < unsigned(n_experts);
+    const int key = ok ? bucket_of(e, sorted, per_segment) : 0;
+    const uint64_t peers = peer_mask(key, ok, nbits);
+    int pos = 0;
+    if (ok) {
+      const int rank = __popcll(peers & lanemask_lt());
+      pos = run[key] + rank;
+      __builtin_amdgcn_wave_barrier();
+      if (rank == 0) run[key] = pos + __popcll(peers);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (ok) {
+      dst_pos[q] = pos;
+      src_pair[pos] = int32_t(q);
+      if (row_expert) row_expert[pos] = e;
+    } else if (in) {
+      dst_pos[q] = -1;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ count
+__global__ __launch_bounds__(kBlock) void count_kernel(const int32_t* __restrict__ idx, int64_t nk,
+                                                       int n_experts, int chunk,
+                                                       int32_t* __restrict__ hist,
+                                                       int32_t* status, int identity,
+                                                       int32_t* __restrict__ dst_pos,
+                                                       int32_t* __restrict__ src_pair,
+                                                       int32_t* __restrict__ row_expert) {
+  __shared__ int h[kMaxExperts];
+  for (int i = threadIdx.x; i < n_experts; i += kBlock) h[i] = 0;
+  __syncthreads();
+  const int64_t q0 = int64_t(blockIdx.x) * chunk;
+  const int64_t q1 = q0 + chunk < nk ? q0 + chunk : nk;
+  bool bad = false;
+  for (int64_t q = q0 + threadIdx.x; q < q1; q += kBlock) {
+    const int e = idx[q];
+    if (unsigned(e) < unsigned(n_experts)) atomicAdd(&h[e], 1);
+    else bad = true;
+    if (identity) {
+      dst_pos[q] = int32_t(q);
+      src_pair[q] = int32_t(q);
+      if (row_expert) row_expert[q] = e;
+    }
+  }
+  if (bad && status) atomicOr(status, 1);
+  __syncthreads();
+  int32_t* out = hist + int64_t(blockIdx.x) * n_experts;
+  for (int i = threadIdx.x; i < n_experts; i += kBlock) out[i] = h[i];
+}
+
+// ------------------------------------------------------------------ scan
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist, int n_chunks,
+                                                    int n_experts, int n_segments, int sorted,
+                                                    int32_t* __restrict__ base,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ seg_offsets) {
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_wave[17];
+  const int tid = threadIdx.x;
+  int c = 0;
+  if (tid < n_experts)
+    for (int p = 0; p < n_chunks; ++p) c += hist[int64_t(p) * n_experts + tid];
+  int total;
+  const int excl = block_exclusive_scan(c, s_wave, &total);
+  if (tid < n_experts) {
+    counts[tid] = c;
+    offsets[tid] = excl;
+    s_off[tid] = excl;
+  }
+  if (tid == 0) {
+    offsets[n_experts] = total;
+    s_off[n_experts] = total;
+  }
+  __syncthreads();
+  const int per = n_experts / n_segments;
+  for (int i = tid; i <= n_segments; i += blockDim.x) seg_offsets[i] = s_off[i * per];
+  if (sorted) {
+    if (tid < n_experts) {
+      int run = s_off[tid];
+      for (int p = 0; p < n_chunks; ++p) {
+        const int v = hist[int64_t(p) * n_experts + tid];
+        base[int64_t(p) * n_experts + tid] = run;
+        run += v;
+      }
+    }
+  } else {
+    const int64_t cells = int64_t(n_chunks) * n_segments;
+    for (int64_t i = tid; i < cells; i += blockDim.x) {
+      const int64_t p = i / n_segments;
+      const int g = int(i - p * n_segments);
+      const int32_t* hp = hist + p * n_experts + int64_t(g) * per;
+      int s = 0;
+      for (int e = 0; e < per; ++e) s += hp[e];
+      base[i] = s;
+    }
+    __syncthreads();
+    if (tid < n_segments) {
+      int run = s_off[tid * per];
+      for (int p = 0; p < n_chunks; ++p) {
+        const int v = base[int64_t(p) * n_segments + tid];
+        base[int64_t(p) * n_segments + tid] = run;
+        run += v;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ rank
+__global__ __launch_bounds__(kBlock) void rank_kernel(const int32_t* __restrict__ idx, int64_t nk,
+                                                      int n_experts, int chunk, int sorted,
+                                                      int per_segment, int n_buckets, int nbits,
+                                                      const int32_t* __restrict__ base,
+                                                      int32_t* __restrict__ dst_pos,
+                                                      int32_t* __restrict__ src_pair,
+                                                      int32_t* __restrict__ row_expert) {
+  constexpr int kWaves = kBlock / kWave;
+  __shared__ int wh[kWaves * kMaxExperts];
+  const int w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  for (int i = threadIdx.x; i < kWaves * n_buckets; i += kBlock) wh[i] = 0;
+  __syncthreads();
+  const int64_t q0 = int64_t(blockIdx.x) * chunk;
+  const int64_t q1 = q0 + chunk < nk ? q0 + chunk : nk;
+  const int sub = chunk / kWaves;
+  const int64_t s0 = q0 + int64_t(w) * sub < q1 ? q0 + int64_t(w) * sub : q1;
+  const int64_t s1 = s0 + sub < q1 ? s0 + sub : q1;
+  int* mine = wh + w * n_buckets;
+  for (int64_t q = s0 + lane; q < s1; q += kWave) {
+    const int e = idx[q];
+    if (unsigned(e) < unsigned(n_experts)) atomicAdd(&mine[bucket_of(e, sorted, per_segment)], 1);
+  }
+  __syncthreads();
+  const int32_t* bp = base + int64_t(blockIdx.x) * n_buckets;
+  for (int b = threadIdx.x; b < n_buckets; b += kBlock) {
+    int run = bp[b];
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const int c = wh[ww * n_buckets + b];
+      wh[ww * n_buckets + b] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  ordered_walk(idx, s0, s1, n_experts, sorted, per_segment, nbits, mine, dst_pos, src_pair,
+               row_expert);
+}
+
+// ------------------------------------------------------------------ small problems
+__global__ __launch_bounds__(kSmallThreads) void small_meta_kernel(
+    const int32_t* __restrict__ idx, int64_t nk, int n_experts, int n_segments, int sorted,
+    int nbits, int identity, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ seg_offsets, int32_t* __restrict__ dst_pos,
+    int32_t* __restrict__ src_pair, int32_t* __restrict__ row_expert, int32_t* status) {
+  __shared__ int h[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int wh[kSmallWaves * kSmallMaxBuckets];
+  __shared__ int s_wave[17];
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = lane_id();
+  const int per = n_experts / n_segments;
+  const int n_buckets = sorted ? n_experts : n_segments;
+  for (int i = tid; i < n_experts; i += kSmallThreads) h[i] = 0;
+  if (!identity)
+    for (int i = tid; i < kSmallWaves * n_buckets; i += kSmallThreads) wh[i] = 0;
+  __syncthreads();
+
+  // wave w owns pairs [s0, s1), a multiple of 64 long
+  const int64_t sub = ((nk + kSmallWaves - 1) / kSmallWaves + kWave - 1) / kWave * kWave;
+  const int64_t s0 = int64_t(w) * sub < nk ? int64_t(w) * sub : nk;
+  const int64_t s1 = s0 + sub < nk ? s0 + sub : nk;
+  int* mine = wh + w * n_buckets;
+  bool bad = false;
+  for (int64_t q = s0 + lane; q < s1; q += kWave) {
+    const int e = idx[q];
+    if (unsigned(e) < unsigned(n_experts)) {
+      atomicAdd(&h[e], 1);
+      if (!identity) atomicAdd(&mine[bucket_of(e, sorted, per)], 1);
+    } else {
+      bad = true;
+    }
+    if (identity) {
+      dst_pos[q] = int32_t(q);
+      src_pair[q] = int32_t(q);
+      if (row_expert) row_expert[q] = e;
+    }
+  }
+  if (bad && status) atomicOr(status, 1);
+  __syncthreads();
+
+  const int c = tid < n_experts ? h[tid] : 0;
+  int total;
+  const int excl = block_exclusive_scan(c, s_wave, &total);
+  if (tid < n_experts) {
+    counts[tid] = c;
+    offsets[tid] = excl;
+    s_off[tid] = excl;
+  }
+  if (tid == 0) {
+    offsets[n_experts] = total;
+    s_off[n_experts] = total;
+  }
+  __syncthreads();
+  for (int i = tid; i <= n_segments; i += blockDim.x) seg_offsets[i] = s_off[i * per];
+  if (identity) return;
+
+  for (int b = tid; b < n_buckets; b += kSmallThreads) {
+    int run = s_off[sorted ? b : b * per];
+    for (int ww = 0; ww < kSmallWaves; ++ww) {
+      const int cc = wh[ww * n_buckets + b];
+      wh[ww * n_buckets + b] = run;
+      run += cc;
+    }
+  }
+  __syncthreads();
+  ordered_walk(idx, s0, s1, n_experts, sorted, per, nbits, mine, dst_pos, src_pair, row_expert);
+}
+
+// ------------------------------------------------------------------ N == 0
+__global__ void zero_offsets_kernel(int n_experts, int n_segments, int32_t* counts,
+                                    int32_t* offsets, int32_t* seg_offsets) {
+  for (int i = threadIdx.x; i <= n_experts; i += blockDim.x) {
+    if (i < n_experts) counts[i] = 0;
+    offsets[i] = 0;
+    if (i <= n_segments) seg_offsets[i] = 0;
+  }
+}
+
+// ------------------------------------------------------------------ row copy
+// One wave per (token, slice) item; each lane moves U vectors of type V.
+template <typename V, int U>
+__global__ __launch_bounds__(kBlock) void scatter_rows_kernel(const V* __restrict__ x,
+                                                              int64_t n_tokens, int64_t nvec,
+                                                              int k, int n_slices,
+                                                              const int32_t* __restrict__ dst_pos,
+                                                              int64_t nk, V* __restrict__ rows) {
+  const int lane = lane_id();
+  const int64_t item = __builtin_amdgcn_readfirstlane(int(blockIdx.x)) * int64_t(kBlock / kWave) +
+                       __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
+  const int64_t t = item / n_slices;
+  if (t >= n_tokens) return;
+  const int64_t v0 = (item - t * n_slices) * int64_t(kWave * U) + lane;
+  const V* src = x + t * nvec;
+  V buf[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (v0 + u * kWave < nvec) buf[u] = src[v0 + u * kWave];
+  const int32_t* dp = dst_pos + t * k;
+  for (int j = 0; j < k; ++j) {
+    const int p = dp[j];
+    if (unsigned(p) >= uint64_t(nk)) continue;
+    V* dst = rows + int64_t(p) * nvec;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * kWave < nvec) dst[v0 + u * kWave] = buf[u];
+  }
+}
+
+template <typename V>
+hipError_t launch_scatter_typed(const void* x, int64_t n_tokens, int64_t row_bytes, int k,
+                                const int32_t* dst_pos, int64_t nk, void* rows,
+                                hipStream_t stream) {
+  constexpr int U = 2;
+  const int64_t nvec = row_bytes / int64_t(sizeof(V));
+  const int n_slices = int((nvec + kWave * U - 1) / (kWave * U));
+  const int64_t items = n_tokens * n_slices;
+  const int per_block = kBlock / kWave;
+  const dim3 grid(unsigned((items + per_block - 1) / per_block));
+  scatter_rows_kernel<V, U><<<grid, kBlock, 0, stream>>>(
+      static_cast<const V*>(x), n_tokens, nvec, k, n_slices, dst_pos, nk, static_cast<V*>(rows));
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const void* x, int64_t n_tokens, int64_t row_bytes, int k,
+                          const int32_t* dst_pos, int64_t nk, void* rows, hipStream_t stream) {
+  // widest access that divides the row size and both base addresses
+  const uint64_t align = uint64_t(row_bytes) | reinterpret_cast<uintptr_t>(x) |
+                         reinterpret_cast<uintptr_t>(rows);
+  if ((align & 15) == 0) return launch_scatter_typed<uint4>(x, n_tokens, row_bytes, k, dst_pos, nk, rows, stream);
+  if ((align & 7) == 0) return launch_scatter_typed<uint2>(x, n_tokens, row_bytes, k, dst_pos, nk, rows, stream);
+  if ((align & 3) == 0) return launch_scatter_typed<uint32_t>(x, n_tokens, row_bytes, k, dst_pos, nk, rows, stream);
+  if ((align & 1) == 0) return launch_scatter_typed<uint16_t>(x, n_tokens, row_bytes, k, dst_pos, nk, rows, stream);
+  return launch_scatter_typed<uint8_t>(x, n_tokens, row_bytes, k, dst_pos, nk, rows, stream);
+}
+
+// Gather form: one wave per (row, slice) item, rows[p] = x[src_pair[p] / k].
+template <typename V, int U>
+__global__ __launch_bounds__(kBlock) void gather_rows_kernel(const V* __restrict__ x,
+                                                             int64_t n_tokens, int64_t nvec,
+                                                             int k, int n_slices,
+                                                             const int32_t* __restrict__ src_pair,
+                                                             int64_t n_rows, V* __restrict__ rows) {
+  const int lane = lane_id();
+  const int64_t item = __builtin_amdgcn_readfirstlane(int(blockIdx.x)) * int64_t(kBlock / kWave) +
+                       __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
+  const int64_t p = item / n_slices;
+  if (p >= n_rows) return;
+  const int64_t v0 = (item - p * n_slices) * int64_t(kWave * U) + lane;
+  const int q = src_pair[p];
+  if (q < 0 || int64_t(q) / k >= n_tokens) return;
+  const V* src = x + (int64_t(q) / k) * nvec;
+  V* dst = rows + p * nvec;
+  V buf[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (v0 + u * kWave < nvec) buf[u] = src[v0 + u * kWave];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (v0 + u * kWave < nvec) dst[v0 + u * kWave] = buf[u];
+}
+
+template <typename V>
+hipError_t launch_gather_typed(const void* x, int64_t n_tokens, int64_t row_bytes, int k,
+                               const int32_t* src_pair, int64_t n_rows, void* rows,
+                               hipStream_t stream) {
+  constexpr int U = 2;
+  const int64_t nvec = row_bytes / int64_t(sizeof(V));
+  const int n_slices = int((nvec + kWave * U - 1) / (kWave * U));
+  const int64_t items = n_rows * n_slices;
+  const int per_block = kBlock / kWave;
+  const dim3 grid(unsigned((items + per_block - 1) / per_block));
+  gather_rows_kernel<V, U><<<grid, kBlock, 0, stream>>>(
+      static_cast<const V*>(x), n_tokens, nvec, k, n_slices, src_pair, n_rows, static_cast<V*>(rows));
+  return hipGetLastError();
+}
+
+int bits_for(int n) {
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+}  // namespace
+
+DispatchPlan plan_dispatch(int64_t n_tokens, int n_experts, int k, int n_segments) {
+  DispatchPlan p{};
+  p.nk = n_tokens * k;
+  int64_t chunk = 1024;
+  if (p.nk > int64_t(1024) * 1024) chunk = ((p.nk + 1023) / 1024 + 255) / 256 * 256;
+  p.chunk = int(chunk);
+  p.n_chunks = int((p.nk + chunk - 1) / chunk);
+  p.small = p.nk <= kSmallMaxPairs && n_experts <= kSmallMaxBuckets ? 1 : 0;
+  (void)n_segments;
+  return p;
+}
+
+size_t dispatch_workspace_bytes(int64_t n_tokens, int n_experts, int k, int n_segments) {
+  const DispatchPlan p = plan_dispatch(n_tokens, n_experts, k, n_segments);
+  const size_t cells = size_t(p.n_chunks > 0 ? p.n_chunks : 1) * size_t(n_experts);
+  return 2 * cells * sizeof(int32_t) + 256;
+}
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
+  const DispatchPlan p = plan_dispatch(a.n_tokens, a.n_experts, a.k, a.n_segments);
+  if (p.nk == 0) {
+    zero_offsets_kernel<<<1, 256, 0, stream>>>(a.n_experts, a.n_segments, a.expert_counts,
+                                               a.expert_offsets, a.segment_offsets);
+    return hipGetLastError();
+  }
+  const int identity = (!a.sorted && a.n_segments == 1) ? 1 : 0;
+  const int per = a.n_experts / a.n_segments;
+  const int n_buckets = a.sorted ? a.n_experts : a.n_segments;
+  const int nbits = bits_for(n_buckets);
+
+  if (p.small) {
+    small_meta_kernel<<<1, kSmallThreads, 0, stream>>>(
+        a.topk_idx, p.nk, a.n_experts, a.n_segments, a.sorted, nbits, identity, a.expert_counts,
+        a.expert_offsets, a.segment_offsets, a.dst_pos, a.src_pair, a.row_expert, a.status);
+  } else {
+    int32_t* hist = static_cast<int32_t*>(a.workspace);
+    int32_t* base = hist + size_t(p.n_chunks) * a.n_experts;
+    count_kernel<<<p.n_chunks, kBlock, 0, stream>>>(a.topk_idx, p.nk, a.n_experts, p.chunk, hist,
+                                                    a.status, identity, a.dst_pos, a.src_pair,
+                                                    a.row_expert);
+    scan_kernel<<<1, 1024, 0, stream>>>(hist, p.n_chunks, a.n_experts, a.n_segments, a.sorted,
+                                        base, a.expert_counts, a.expert_offsets,
+                                        a.segment_offsets);
+    if (!identity)
+      rank_kernel<<<p.n_chunks, kBlock, 0, stream>>>(a.topk_idx, p.nk, a.n_experts, p.chunk,
+                                                     a.sorted, per, n_buckets, nbits, base,
+                                                     a.dst_pos, a.src_pair, a.row_expert);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (a.x) {
+    err = launch_scatter(a.x, a.n_tokens, a.row_bytes, a.k, a.dst_pos, p.nk, a.rows, stream);
+    if (err != hipSuccess) return err;
+  }
+  if (a.x_scales) {
+    err = launch_scatter(a.x_scales, a.n_tokens, a.scale_bytes, a.k, a.dst_pos, p.nk,
+                         a.row_scales, stream);
+  }
+  return err;
+}
+
+hipError_t launch_scatter_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int k,
+                               const int32_t* dst_pos, void* rows, hipStream_t stream) {
+  return launch_scatter(x, n_tokens, row_bytes, k, dst_pos, n_tokens * k, rows, stream);
+}
+
+hipError_t launch_gather_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int k,
+                              const int32_t* src_pair, int64_t n_rows, void* rows,
+                              hipStream_t stream) {
+  const uint64_t align = uint64_t(row_bytes) | reinterpret_cast<uintptr_t>(x) |
+                         reinterpret_cast<uintptr_t>(rows);
+  if ((align & 15) == 0) return launch_gather_typed<uint4>(x, n_tokens, row_bytes, k, src_pair, n_rows, rows, stream);
+  if ((align & 7) == 0) return launch_gather_typed<uint2>(x, n_tokens, row_bytes, k, src_pair, n_rows, rows, stream);
+  if ((align & 3) == 0) return launch_gather_typed<uint32_t>(x, n_tokens, row_bytes, k, src_pair, n_rows, rows, stream);
+  if ((align & 1) == 0) return launch_gather_typed<uint16_t>(x, n_tokens, row_bytes, k, src_pair, n_rows, rows, stream);
+  return launch_gather_typed<uint8_t>(x, n_tokens, row_bytes, k, src_pair, n_rows, rows, stream);
+}
+
+}  // namespace moe

@@ -1,0 +1,74 @@
+// Host-side launchers of the MoE kernels.  Argument checking happens in
+// api.cpp before any of these is called; the launchers only shape grids.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+
+hipError_t launch_route_topk(const float* logits, int64_t n_tokens, int n_experts, int k,
+                             int renormalize, int32_t* topk_idx, float* topk_w,
+                             hipStream_t stream);
+
+// ---- dispatch
+struct DispatchPlan {
+  int64_t nk;          // routed pairs
+  int chunk;           // pairs per counting chunk (multiple of 256)
+  int n_chunks;        // P
+  int small;           // 1: one workgroup computes counts, scan and positions
+};
+
+DispatchPlan plan_dispatch(int64_t n_tokens, int n_experts, int k, int n_segments);
+size_t dispatch_workspace_bytes(int64_t n_tokens, int n_experts, int k, int n_segments);
+
+struct DispatchArgs {
+  const void* x;
+  const float* x_scales;
+  int64_t row_bytes;        // D * element size
+  int64_t scale_bytes;      // D/128 * 4 for F8, else 0
+  int64_t n_tokens;
+  const int32_t* topk_idx;
+  int n_experts, k, n_segments, sorted;
+  void* rows;
+  float* row_scales;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* segment_offsets;
+  int32_t* src_pair;
+  int32_t* dst_pos;
+  int32_t* row_expert;
+  void* workspace;
+  int32_t* status;          // device word set to 1 on an out-of-range id, or null
+};
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
+
+// Row copies on their own (byte payloads): scatter form rows[dst_pos[q]] =
+// x[q / k] and gather form rows[p] = x[src_pair[p] / k].
+hipError_t launch_scatter_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int k,
+                               const int32_t* dst_pos, void* rows, hipStream_t stream);
+hipError_t launch_gather_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int k,
+                              const int32_t* src_pair, int64_t n_rows, void* rows,
+                              hipStream_t stream);
+
+// ---- combine
+hipError_t launch_combine(const void* y, int y_bf16, int64_t n_tokens, int64_t hidden, int k,
+                          const int32_t* dst_pos, const float* topk_w, void* out, int out_bf16,
+                          hipStream_t stream);
+
+// ---- experts
+hipError_t launch_dequant_rows(const uint8_t* rows, const float* row_scales, int64_t n_rows,
+                               int64_t hidden, uint16_t* y, hipStream_t stream);
+
+size_t grouped_swiglu_workspace_bytes(int64_t n_rows, int n_experts, int64_t hidden, int64_t ffn);
+hipError_t launch_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
+                                 const int32_t* expert_offsets, int n_experts, const void* w_gate,
+                                 const void* w_up, const void* w_down, int64_t ffn, void* y,
+                                 void* workspace, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,73 @@
+"""Helpers for GPU tests: numpy <-> device tensors and the tolerance checks.
+
+The tolerances follow from the arithmetic (derivation in the design doc):
+* fp32 combine output: |g - o| <= 1e-6 * sum_j |w_j y_j| (a k-term fp32 FMA
+  chain is within gamma_k * sum|terms|, gamma_8 ~ 4.8e-7);
+* bf16 combine output: within one bf16 ulp of the correctly rounded exact
+  value, or, where the terms cancel, within the fp32 bound plus half a bf16
+  ulp of the result;
+* routing weights: 1e-6 relative (a handful of fp32 roundings plus expf).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import codecs
+
+DEV = "cuda:0"
+
+
+def to_dev(a: np.ndarray, kind: str | None = None) -> torch.Tensor:
+    """float32 -> float32; uint16 bf16 bits -> bfloat16; uint8 -> uint8; int32 -> int32."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
+    return t.cpu().numpy()
+
+
+def as_f32(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns or float arrays -> float32 values."""
+    return codecs.bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float32)
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    a = np.maximum(np.abs(np.asarray(v, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def check_combine(got: np.ndarray, exact: np.ndarray, abs_terms: np.ndarray, out_bf16: bool,
+                  what: str = "") -> None:
+    """got: device output (float32 or bf16 bits); exact: float64 oracle value;
+    abs_terms: float64 sum_j |w_j y_j| per element."""
+    if not out_bf16:
+        err = np.abs(got.astype(np.float64) - exact)
+        bound = 1e-6 * abs_terms
+        bad = err > bound
+        assert not bad.any(), f"{what}: {bad.sum()} fp32 elements outside 1e-6*sum|terms|, " \
+                              f"worst {np.max(err - bound):.3e}"
+        return
+    g = codecs.bf16_bits_to_f32(got).astype(np.float64)
+    r = codecs.bf16_bits_to_f32(codecs.f64_to_bf16_bits(exact)).astype(np.float64)
+    one_ulp = np.abs(g - r) <= bf16_ulp(np.maximum(np.abs(g), np.abs(r)))
+    cancel_ok = np.abs(g - exact) <= 1e-6 * abs_terms + 0.5 * bf16_ulp(g)
+    bad = ~(one_ulp | cancel_ok)
+    assert not bad.any(), f"{what}: {bad.sum()} bf16 elements beyond 1 ulp"
+
+
+def combine_reference(y_rows_f32: np.ndarray, dst_pos: np.ndarray, w: np.ndarray, k: int,
+                      tokens=None):
+    """(exact value, sum of |terms|) from the oracle for the given tokens."""
+    from oracle.combine import combine_f64
+    exact = combine_f64(y_rows_f32, dst_pos, w, k, tokens=tokens)
+    mag = combine_f64(np.abs(y_rows_f32), dst_pos, np.abs(w), k, tokens=tokens)
+    return exact, mag

@@ -1,0 +1,139 @@
+"""The C ABI library loads, exports every declared symbol and rejects bad
+arguments before touching the GPU (CPU only: no call here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_moe_route_topk_amd import _lib
+from oracle.dispatch import resolve_sorted as oracle_resolve_sorted
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_dc.h")
+lib = _lib.lib
+ARG, UNSUP, WS = _lib.MOE_ERR_ARG, _lib.MOE_ERR_UNSUPPORTED, _lib.MOE_ERR_WORKSPACE
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), name
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures must mirror the header"
+
+
+def test_version_and_error_string():
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_route_topk(None, 4, 8, 0, 1, None, None, None) == ARG
+    assert b"k" in lib.moe_last_error()
+    out = ctypes.c_int32()
+    assert lib.moe_resolve_sorted(1, 5, 1, ctypes.byref(out)) == 0
+    assert lib.moe_last_error() == b""
+
+
+@pytest.mark.parametrize("sort", [-1, 0, 1])
+@pytest.mark.parametrize("n", [0, 1, 2, 127, 128, 129, 256, 257, 4096])
+@pytest.mark.parametrize("cutoff", [-3, 0, 1, 128, 256])
+def test_resolve_sorted_matches_oracle(sort, n, cutoff):
+    out = ctypes.c_int32(-1)
+    assert lib.moe_resolve_sorted(sort, n, cutoff, ctypes.byref(out)) == 0
+    assert bool(out.value) == oracle_resolve_sorted(sort, n, cutoff)
+
+
+def test_resolve_sorted_errors():
+    out = ctypes.c_int32()
+    assert lib.moe_resolve_sorted(2, 5, 1, ctypes.byref(out)) == ARG
+    assert lib.moe_resolve_sorted(1, -1, 1, ctypes.byref(out)) == ARG
+    assert lib.moe_resolve_sorted(1, 5, 1, None) == ARG
+
+
+def test_route_errors():
+    f = lib.moe_route_topk
+    assert f(FAKE, -1, 8, 2, 1, FAKE, FAKE, None) == ARG
+    assert f(FAKE, 4, 0, 1, 1, FAKE, FAKE, None) == ARG
+    assert f(FAKE, 4, 8, 9, 1, FAKE, FAKE, None) == ARG
+    assert f(FAKE, 4, 2048, 8, 1, FAKE, FAKE, None) == UNSUP
+    assert f(FAKE, 4, 64, 33, 1, FAKE, FAKE, None) == UNSUP
+    assert f(None, 4, 8, 2, 1, FAKE, FAKE, None) == ARG
+    assert f(FAKE, 4, 8, 2, 1, None, FAKE, None) == ARG
+    assert f(None, 0, 8, 2, 1, None, None, None) == 0          # N == 0: no-op, no launch
+
+
+def test_workspace_sizing():
+    f = lib.moe_dispatch_workspace_bytes
+    assert f(4096, 256, 8, 1) > 0
+    assert f(4096, 256, 8, 8) == f(4096, 256, 8, 1) or f(4096, 256, 8, 8) > 0
+    assert f(0, 8, 2, 1) > 0
+    for bad in ((-1, 8, 2, 1), (4, 0, 1, 1), (4, 8, 9, 1), (4, 8, 2, 3), (4, 8, 2, 0),
+                (4, 2048, 2, 1), (2**31, 8, 2, 1)):
+        assert f(*bad) == 0, bad
+    # grows with the number of chunks
+    assert f(1 << 20, 256, 8, 1) > f(4096, 256, 8, 1)
+    assert lib.moe_grouped_swiglu_workspace_bytes(16384, 8, 4096, 14336) >= 16384 * 14336 * 2
+
+
+def _dispatch(**kw):
+    a = dict(x=FAKE, x_scales=None, dtype=1, n=4, d=64, idx=FAKE, e=8, k=2, g=1, sort=1,
+             cutoff=256, used=None, rows=FAKE, row_scales=None, counts=FAKE, offs=FAKE,
+             segs=FAKE, src=FAKE, dst=FAKE, rexp=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return lib.moe_dispatch(a["x"], a["x_scales"], a["dtype"], a["n"], a["d"], a["idx"], a["e"],
+                            a["k"], a["g"], a["sort"], a["cutoff"], a["used"], a["rows"],
+                            a["row_scales"], a["counts"], a["offs"], a["segs"], a["src"],
+                            a["dst"], a["rexp"], a["ws"], a["wsb"], None)
+
+
+def test_dispatch_errors():
+    assert _dispatch(n=-1) == ARG
+    assert _dispatch(k=9) == ARG
+    assert _dispatch(e=2048) == UNSUP
+    assert _dispatch(k=40, e=64) == UNSUP
+    assert _dispatch(g=3) == ARG
+    assert _dispatch(g=0) == ARG
+    assert _dispatch(d=0) == ARG
+    assert _dispatch(dtype=7) == ARG
+    assert _dispatch(sort=5) == ARG
+    assert _dispatch(rows=None) == ARG                     # x without rows
+    assert _dispatch(x=None) == ARG                        # rows without x
+    assert _dispatch(dtype=2, d=100) == ARG                # F8 needs D % 128 == 0
+    assert _dispatch(dtype=2, d=128) == ARG                # F8 needs scales
+    assert _dispatch(x_scales=FAKE, row_scales=FAKE) == ARG   # scales only for F8
+    assert _dispatch(counts=None) == ARG
+    assert _dispatch(src=None) == ARG
+    assert _dispatch(idx=None) == ARG
+    assert _dispatch(ws=None) == WS
+    assert _dispatch(wsb=16) == WS
+    assert _dispatch(ws=ctypes.c_void_p(0x1004)) == WS     # misaligned
+    assert _dispatch(n=2**30, k=4, e=8) == UNSUP           # NK beyond int32
+
+
+def test_combine_errors():
+    f = lib.moe_combine
+    assert f(FAKE, 1, -1, 64, 2, FAKE, FAKE, FAKE, 1, None) == ARG
+    assert f(FAKE, 1, 4, 0, 2, FAKE, FAKE, FAKE, 1, None) == ARG
+    assert f(FAKE, 1, 4, 64, 0, FAKE, FAKE, FAKE, 1, None) == ARG
+    assert f(FAKE, 1, 4, 64, 33, FAKE, FAKE, FAKE, 1, None) == UNSUP
+    assert f(FAKE, 2, 4, 64, 2, FAKE, FAKE, FAKE, 1, None) == ARG   # F8 y not accepted
+    assert f(FAKE, 1, 4, 64, 2, FAKE, FAKE, FAKE, 5, None) == ARG
+    assert f(None, 1, 4, 64, 2, FAKE, FAKE, FAKE, 1, None) == ARG
+    assert f(None, 1, 0, 64, 2, None, None, None, 1, None) == 0      # N == 0
+
+
+def test_dequant_and_swiglu_errors():
+    assert lib.moe_dequant_rows(FAKE, FAKE, 4, 100, FAKE, None) == ARG
+    assert lib.moe_dequant_rows(None, FAKE, 4, 128, FAKE, None) == ARG
+    assert lib.moe_dequant_rows(ctypes.c_void_p(0x1001), FAKE, 4, 128, FAKE, None) == ARG
+    g = lib.moe_grouped_swiglu
+    assert g(FAKE, 16, 100, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 30, None) == UNSUP
+    assert g(FAKE, -1, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 30, None) == ARG
+    assert g(None, 16, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 30, None) == ARG
+    assert g(FAKE, 16, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 16, None) == WS
