@@ -9,7 +9,7 @@
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
-constexpr int kMaxTopK = 32;
+constexpr int kMaxTopK = 64;
 
 hipError_t launch_route_topk(const float* logits, int64_t n_tokens, int n_experts, int k,
                              int renormalize, int32_t* topk_idx, float* topk_w,

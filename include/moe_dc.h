@@ -83,7 +83,7 @@ enum { MOE_SORT_AUTO = -1, MOE_SORT_OFF = 0, MOE_SORT_ON = 1 };
 
 /* Limits of this implementation. */
 #define MOE_MAX_EXPERTS 1024
-#define MOE_MAX_TOPK 32
+#define MOE_MAX_TOPK 64
 
 /* ABI version (MOE_DC_ABI_VERSION of the built library). */
 int moe_abi_version(void);

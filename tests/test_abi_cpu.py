@@ -62,7 +62,7 @@ def test_route_errors():
     assert f(FAKE, 4, 0, 1, 1, FAKE, FAKE, None) == ARG
     assert f(FAKE, 4, 8, 9, 1, FAKE, FAKE, None) == ARG
     assert f(FAKE, 4, 2048, 8, 1, FAKE, FAKE, None) == UNSUP
-    assert f(FAKE, 4, 64, 33, 1, FAKE, FAKE, None) == UNSUP
+    assert f(FAKE, 4, 128, 65, 1, FAKE, FAKE, None) == UNSUP
     assert f(None, 4, 8, 2, 1, FAKE, FAKE, None) == ARG
     assert f(FAKE, 4, 8, 2, 1, None, FAKE, None) == ARG
     assert f(None, 0, 8, 2, 1, None, None, None) == 0          # N == 0: no-op, no launch
@@ -96,7 +96,7 @@ def test_dispatch_errors():
     assert _dispatch(n=-1) == ARG
     assert _dispatch(k=9) == ARG
     assert _dispatch(e=2048) == UNSUP
-    assert _dispatch(k=40, e=64) == UNSUP
+    assert _dispatch(k=65, e=128) == UNSUP
     assert _dispatch(g=3) == ARG
     assert _dispatch(g=0) == ARG
     assert _dispatch(d=0) == ARG
@@ -121,7 +121,7 @@ def test_combine_errors():
     assert f(FAKE, 1, -1, 64, 2, FAKE, FAKE, FAKE, 1, None) == ARG
     assert f(FAKE, 1, 4, 0, 2, FAKE, FAKE, FAKE, 1, None) == ARG
     assert f(FAKE, 1, 4, 64, 0, FAKE, FAKE, FAKE, 1, None) == ARG
-    assert f(FAKE, 1, 4, 64, 33, FAKE, FAKE, FAKE, 1, None) == UNSUP
+    assert f(FAKE, 1, 4, 64, 65, FAKE, FAKE, FAKE, 1, None) == UNSUP
     assert f(FAKE, 2, 4, 64, 2, FAKE, FAKE, FAKE, 1, None) == ARG   # F8 y not accepted
     assert f(FAKE, 1, 4, 64, 2, FAKE, FAKE, FAKE, 5, None) == ARG
     assert f(None, 1, 4, 64, 2, FAKE, FAKE, FAKE, 1, None) == ARG
