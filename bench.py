@@ -126,6 +126,28 @@ def time_path(path, steps, warmup):
     return wall / steps * 1e3, stage.mean(axis=0) * 1e3, np.median(stage, axis=0) * 1e3
 
 
+def time_graph(path, steps, warmup):
+    """The same step captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: removes host launch overhead, which dominates at decode size."""
+    torch = path.torch
+    path.step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path.step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def check_outputs(path):
     """Spot-check the timed buffers against the oracle (a few tokens)."""
     from oracle import codecs
@@ -257,6 +279,8 @@ def main():
         "stages_us": {nm: round(float(v), 2) for nm, v in zip(names, stage_mean_us)},
         "roofline": roofline,
     }
+    rec["us_per_layer_hipgraph"] = round(time_graph(path, args.steps, args.warmup) * 1e3, 2)
+    check_outputs(path)
     if not args.no_decode and args.workload == "prefill":
         dcfg = CONFIGS["decode"]
         dpath = Path(dcfg, torch, moe)
@@ -264,7 +288,10 @@ def main():
         check_outputs(dpath)
         db = algorithmic_bytes(dcfg.n_tokens, dcfg.hidden, dcfg.n_experts, dcfg.top_k,
                                dcfg.n_segments, dcfg.elem_bytes)
+        gms = time_graph(dpath, max(args.steps, 200), args.warmup)
+        check_outputs(dpath)
         rec["decode"] = {"workload": f"decode: {dcfg.note}", "us_per_layer": round(dms * 1e3, 2),
+                         "us_per_layer_hipgraph": round(gms * 1e3, 2),
                          "GB_per_s": round(db["total"] / (dms * 1e-3) / 1e9, 1),
                          "cache": "hot (33 MB of buffers stay in the 256 MB last-level cache)",
                          "stages_us": {nm: round(float(v), 2) for nm, v in zip(names, dst_us)}}

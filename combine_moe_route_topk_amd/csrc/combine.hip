@@ -22,7 +22,6 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kGroup = 8;          // elements per lane per load group
-constexpr int kBatch = 8;          // slots whose loads are issued together
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {   // a group of 8 floats is two 16-byte loads
@@ -61,8 +60,46 @@ template <> struct Elem<uint16_t> {   // bfloat16 bit patterns
 };
 
 // Vector path: D % 8 == 0 and 16-byte aligned rows.  Each lane owns U groups
-// of 8 consecutive elements; a slice is 64 * U groups.
-template <typename TY, typename TO, int U>
+// of 8 consecutive elements; a slice is 64 * U groups.  Slots are taken KB at
+// a time: all KB * U row loads of a batch are issued back to back from
+// clamped (always valid) addresses, and slots that do not exist or carry an
+// out-of-range position are masked out of the FMA chain instead of branched
+// around, so no load waits for another.
+// Row loads are non-temporal: each expert-output row is read exactly once.
+// Measured on MI355X at the prefill shape, this keeps the combine from
+// evicting the just-dispatched rows that are still dirty in the last-level
+// cache through ordinary allocations, and cut the dispatch + combine pair
+// from ~240 us to ~190 us.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 load_stream(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+}
+
+template <typename TY> struct Raw;
+template <> struct Raw<uint16_t> {
+  u32x4 v;
+  __device__ void load(const uint16_t* row, int64_t g) { v = load_stream(row + 8 * g); }
+  __device__ void to_f32(float (&o)[kGroup]) const {
+    unpack_bf16x2(v.x, o[0], o[1]); unpack_bf16x2(v.y, o[2], o[3]);
+    unpack_bf16x2(v.z, o[4], o[5]); unpack_bf16x2(v.w, o[6], o[7]);
+  }
+};
+template <> struct Raw<float> {
+  u32x4 a, b;
+  __device__ void load(const float* row, int64_t g) {
+    a = load_stream(row + 8 * g);
+    b = load_stream(row + 8 * g + 4);
+  }
+  __device__ void to_f32(float (&o)[kGroup]) const {
+    o[0] = __uint_as_float(a.x); o[1] = __uint_as_float(a.y);
+    o[2] = __uint_as_float(a.z); o[3] = __uint_as_float(a.w);
+    o[4] = __uint_as_float(b.x); o[5] = __uint_as_float(b.y);
+    o[6] = __uint_as_float(b.z); o[7] = __uint_as_float(b.w);
+  }
+};
+
+template <typename TY, typename TO, int U, int KB>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const TY* __restrict__ y, int64_t n_tokens,
                                                          int64_t hidden, int k, int n_slices,
                                                          const int32_t* __restrict__ dst_pos,
@@ -75,6 +112,13 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const TY* __restrict__ 
   if (t >= n_tokens) return;
   const int64_t ngroups = hidden / kGroup;
   const int64_t g0 = (item - t * n_slices) * int64_t(kWave * U) + lane;
+  int64_t gi[U];
+  bool gok[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    gok[u] = g0 + u * kWave < ngroups;
+    gi[u] = gok[u] ? g0 + u * kWave : ngroups - 1;
+  }
 
   float acc[U][kGroup];
 #pragma unroll
@@ -82,38 +126,45 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const TY* __restrict__ 
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) acc[u][i] = 0.f;
 
-  const int32_t* dp = dst_pos + t * k;
-  const float* wp = topk_w + t * k;
-  for (int j0 = 0; j0 < k; j0 += kBatch) {
-    float v[kBatch][U][kGroup];
-    bool use[kBatch];
-    float wj[kBatch];
+  // lane j < k holds slot j's position and weight; slots are read with readlane
+  const int my_p = lane < k ? dst_pos[t * k + lane] : -1;
+  const float my_w = lane < k ? topk_w[t * k + lane] : 0.f;
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    Raw<TY> raw[KB][U];
+    const TY* row[KB];
+    bool use[KB];
+    float wj[KB];
 #pragma unroll
-    for (int jj = 0; jj < kBatch; ++jj) {
-      const int j = j0 + jj;
-      const int p = j < k ? dp[j] : -1;
+    for (int jj = 0; jj < KB; ++jj) {
+      const int p = __builtin_amdgcn_readlane(my_p, j0 + jj);   // -1 past the last slot
       use[jj] = unsigned(p) < uint64_t(nk);
-      wj[jj] = j < k ? wp[j] : 0.f;
-      if (use[jj]) {
-        const TY* row = y + int64_t(p) * hidden;
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (g0 + u * kWave < ngroups) Elem<TY>::load(row, g0 + u * kWave, v[jj][u]);
-      }
+      wj[jj] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), j0 + jj));
+      row[jj] = y + int64_t(use[jj] ? p : 0) * hidden;
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int jj = 0; jj < kBatch; ++jj) {
-      if (!use[jj]) continue;
+    for (int jj = 0; jj < KB; ++jj)
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) raw[jj][u].load(row[jj], gi[u]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) acc[u][i] = __builtin_fmaf(wj[jj], v[jj][u][i], acc[u][i]);
+    for (int jj = 0; jj < KB; ++jj) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float v[kGroup];
+        raw[jj][u].to_f32(v);
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+          const float f = __builtin_fmaf(wj[jj], v[i], acc[u][i]);
+          acc[u][i] = use[jj] ? f : acc[u][i];
+        }
+      }
     }
   }
   TO* orow = out + t * hidden;
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    if (g0 + u * kWave < ngroups) Elem<TO>::store(orow, g0 + u * kWave, acc[u]);
+    if (gok[u]) Elem<TO>::store(orow, gi[u], acc[u]);
 }
 
 // Scalar path for any D: one element per lane, a slice is 64 elements.
@@ -150,9 +201,17 @@ hipError_t launch_combine_typed(const void* y, int64_t n_tokens, int64_t hidden,
     const int64_t ngroups = hidden / kGroup;
     const int n_slices = int((ngroups + kWave * U - 1) / (kWave * U));
     const int64_t items = n_tokens * n_slices;
-    combine_kernel<TY, TO, U><<<unsigned((items + per_block - 1) / per_block), kBlock, 0, stream>>>(
-        static_cast<const TY*>(y), n_tokens, hidden, k, n_slices, dst_pos, topk_w, nk,
-        static_cast<TO*>(out));
+    const unsigned blocks = unsigned((items + per_block - 1) / per_block);
+    const TY* yy = static_cast<const TY*>(y);
+    TO* oo = static_cast<TO*>(out);
+    if (k >= 8)
+      combine_kernel<TY, TO, U, 8><<<blocks, kBlock, 0, stream>>>(yy, n_tokens, hidden, k, n_slices, dst_pos, topk_w, nk, oo);
+    else if (k >= 4)
+      combine_kernel<TY, TO, U, 4><<<blocks, kBlock, 0, stream>>>(yy, n_tokens, hidden, k, n_slices, dst_pos, topk_w, nk, oo);
+    else if (k >= 2)
+      combine_kernel<TY, TO, U, 2><<<blocks, kBlock, 0, stream>>>(yy, n_tokens, hidden, k, n_slices, dst_pos, topk_w, nk, oo);
+    else
+      combine_kernel<TY, TO, U, 1><<<blocks, kBlock, 0, stream>>>(yy, n_tokens, hidden, k, n_slices, dst_pos, topk_w, nk, oo);
   } else {
     const int n_slices = int((hidden + kWave - 1) / kWave);
     const int64_t items = n_tokens * n_slices;

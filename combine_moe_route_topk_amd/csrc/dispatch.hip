@@ -12,14 +12,14 @@
 // A stable counting sort without global atomics, so positions are
 // deterministic:
 //   count  -- each chunk of C pairs builds its expert histogram in LDS;
-//   scan   -- one workgroup turns the [P, E] histograms into expert offsets,
-//             segment offsets and per-(chunk, bucket) starting positions in
-//             (bucket-major, chunk-minor) order;
-//   rank   -- each chunk recounts per wave, then each wave walks its pairs in
-//             order, 64 at a time: ballots over the key bits give every lane
-//             the set of lanes with the same bucket, so its rank among
-//             earlier equal keys is a popcount (wave multisplit, after
-//             Ashkiani et al., "GPU Multisplit", PPoPP 2016);
+//   rank   -- each chunk reads all [P, E] histograms (L2-resident), scans the
+//             expert totals into offsets and forms its starting position in
+//             every bucket (bucket-major, chunk-minor order); it recounts per
+//             wave, then each wave walks its pairs in order, 64 at a time:
+//             ballots over the key bits give every lane the set of lanes with
+//             the same bucket, so its rank among earlier equal keys is a
+//             popcount (wave multisplit, after Ashkiani et al., "GPU
+//             Multisplit", PPoPP 2016);
 //   copy   -- scatter form: one wave reads a slice of token t's row once and
 //             writes it to the k destination rows dst_pos[t*k + j].
 // Small problems (NK <= 16384, at most 256 buckets) run count, scan and rank
@@ -83,36 +83,67 @@ __device__ __forceinline__ uint64_t peer_mask(int key, bool active, int nbits) {
 }
 
 // Walk pairs [s0, s1) in order, 64 at a time, assigning positions from the
-// per-bucket running counters run[] (LDS, private to this wave).
+// per-bucket running counters run[] (LDS, private to this wave).  Keys are
+// fetched four steps ahead so their loads overlap.
 __device__ __forceinline__ void ordered_walk(const int32_t* __restrict__ idx, int64_t s0,
                                              int64_t s1, int n_experts, int sorted,
                                              int per_segment, int nbits, int* run,
                                              int32_t* __restrict__ dst_pos,
                                              int32_t* __restrict__ src_pair,
                                              int32_t* __restrict__ row_expert) {
+  constexpr int kAhead = 4;
   const int lane = lane_id();
-  for (int64_t qb = s0; qb < s1; qb += kWave) {
-    const int64_t q = qb + lane;
-    const bool in = q < s1;
-    const int e = in ? idx[q] : -1;
-    const bool ok = in && unsigned(e) < unsigned(n_experts);
-    const int key = ok ? bucket_of(e, sorted, per_segment) : 0;
-    const uint64_t peers = peer_mask(key, ok, nbits);
-    int pos = 0;
-    if (ok) {
-      const int rank = __popcll(peers & lanemask_lt());
-      pos = run[key] + rank;
+  for (int64_t qa = s0; qa < s1; qa += kAhead * kWave) {
+    int ev[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      const int64_t q = qa + i * kWave + lane;
+      ev[i] = q < s1 ? idx[q] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      const int64_t q = qa + i * kWave + lane;
+      if (qa + i * kWave >= s1) break;                  // uniform
+      const bool in = q < s1;
+      const int e = ev[i];
+      const bool ok = in && unsigned(e) < unsigned(n_experts);
+      const int key = ok ? bucket_of(e, sorted, per_segment) : 0;
+      const uint64_t peers = peer_mask(key, ok, nbits);
+      int pos = 0;
+      if (ok) {
+        const int rank = __popcll(peers & lanemask_lt());
+        pos = run[key] + rank;
+        __builtin_amdgcn_wave_barrier();
+        if (rank == 0) run[key] = pos + __popcll(peers);
+      }
       __builtin_amdgcn_wave_barrier();
-      if (rank == 0) run[key] = pos + __popcll(peers);
+      if (ok) {
+        dst_pos[q] = pos;
+        src_pair[pos] = int32_t(q);
+        if (row_expert) row_expert[pos] = e;
+      } else if (in) {
+        dst_pos[q] = -1;
+      }
     }
-    __builtin_amdgcn_wave_barrier();
-    if (ok) {
-      dst_pos[q] = pos;
-      src_pair[pos] = int32_t(q);
-      if (row_expert) row_expert[pos] = e;
-    } else if (in) {
-      dst_pos[q] = -1;
+  }
+}
+
+// Per-wave bucket counts of pairs [s0, s1) into cnt[] (LDS atomics: counts do
+// not depend on order).
+__device__ __forceinline__ void wave_count(const int32_t* __restrict__ idx, int64_t s0, int64_t s1,
+                                           int n_experts, int sorted, int per_segment, int* cnt) {
+  constexpr int kAhead = 4;
+  const int lane = lane_id();
+  for (int64_t qa = s0; qa < s1; qa += kAhead * kWave) {
+    int ev[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      const int64_t q = qa + i * kWave + lane;
+      ev[i] = q < s1 ? idx[q] : -1;
     }
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i)
+      if (unsigned(ev[i]) < unsigned(n_experts)) atomicAdd(&cnt[bucket_of(ev[i], sorted, per_segment)], 1);
   }
 }
 
@@ -130,14 +161,26 @@ __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t* __restrict
   const int64_t q0 = int64_t(blockIdx.x) * chunk;
   const int64_t q1 = q0 + chunk < nk ? q0 + chunk : nk;
   bool bad = false;
-  for (int64_t q = q0 + threadIdx.x; q < q1; q += kBlock) {
-    const int e = idx[q];
-    if (unsigned(e) < unsigned(n_experts)) atomicAdd(&h[e], 1);
-    else bad = true;
-    if (identity) {
-      dst_pos[q] = int32_t(q);
-      src_pair[q] = int32_t(q);
-      if (row_expert) row_expert[q] = e;
+  constexpr int kAhead = 4;
+  for (int64_t qa = q0; qa < q1; qa += kAhead * kBlock) {
+    int ev[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      const int64_t q = qa + i * kBlock + threadIdx.x;
+      ev[i] = q < q1 ? idx[q] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      const int64_t q = qa + i * kBlock + threadIdx.x;
+      if (q >= q1) continue;
+      const int e = ev[i];
+      if (unsigned(e) < unsigned(n_experts)) atomicAdd(&h[e], 1);
+      else bad = true;
+      if (identity) {
+        dst_pos[q] = int32_t(q);
+        src_pair[q] = int32_t(q);
+        if (row_expert) row_expert[q] = e;
+      }
     }
   }
   if (bad && status) atomicOr(status, 1);
@@ -146,102 +189,122 @@ __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t* __restrict
   for (int i = threadIdx.x; i < n_experts; i += kBlock) out[i] = h[i];
 }
 
-// ------------------------------------------------------------------ scan
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist, int n_chunks,
-                                                    int n_experts, int n_segments, int sorted,
-                                                    int32_t* __restrict__ base,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ seg_offsets) {
-  __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_wave[17];
-  const int tid = threadIdx.x;
-  int c = 0;
-  if (tid < n_experts)
-    for (int p = 0; p < n_chunks; ++p) c += hist[int64_t(p) * n_experts + tid];
-  int total;
-  const int excl = block_exclusive_scan(c, s_wave, &total);
-  if (tid < n_experts) {
-    counts[tid] = c;
-    offsets[tid] = excl;
-    s_off[tid] = excl;
-  }
-  if (tid == 0) {
-    offsets[n_experts] = total;
-    s_off[n_experts] = total;
-  }
-  __syncthreads();
-  const int per = n_experts / n_segments;
-  for (int i = tid; i <= n_segments; i += blockDim.x) seg_offsets[i] = s_off[i * per];
-  if (sorted) {
-    if (tid < n_experts) {
-      int run = s_off[tid];
-      for (int p = 0; p < n_chunks; ++p) {
-        const int v = hist[int64_t(p) * n_experts + tid];
-        base[int64_t(p) * n_experts + tid] = run;
-        run += v;
-      }
-    }
-  } else {
-    const int64_t cells = int64_t(n_chunks) * n_segments;
-    for (int64_t i = tid; i < cells; i += blockDim.x) {
-      const int64_t p = i / n_segments;
-      const int g = int(i - p * n_segments);
-      const int32_t* hp = hist + p * n_experts + int64_t(g) * per;
-      int s = 0;
-      for (int e = 0; e < per; ++e) s += hp[e];
-      base[i] = s;
-    }
-    __syncthreads();
-    if (tid < n_segments) {
-      int run = s_off[tid * per];
-      for (int p = 0; p < n_chunks; ++p) {
-        const int v = base[int64_t(p) * n_segments + tid];
-        base[int64_t(p) * n_segments + tid] = run;
-        run += v;
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------ rank
+// Block p owns chunk p.  From the [P, E] chunk histograms (L2-resident) it
+// derives every expert's total and the count in chunks before its own, scans
+// the totals into expert offsets (block 0 also writes counts and offsets),
+// forms its per-bucket starting positions, recounts per wave and walks its
+// pairs in order.
 __global__ __launch_bounds__(kBlock) void rank_kernel(const int32_t* __restrict__ idx, int64_t nk,
-                                                      int n_experts, int chunk, int sorted,
-                                                      int per_segment, int n_buckets, int nbits,
-                                                      const int32_t* __restrict__ base,
+                                                      int n_experts, int n_segments, int chunk,
+                                                      int n_chunks, int sorted, int identity,
+                                                      int nbits,
+                                                      const int32_t* __restrict__ hist,
+                                                      int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ seg_offsets,
                                                       int32_t* __restrict__ dst_pos,
                                                       int32_t* __restrict__ src_pair,
                                                       int32_t* __restrict__ row_expert) {
   constexpr int kWaves = kBlock / kWave;
+  constexpr int kPer = kMaxExperts / kBlock;           // experts per thread in the scan
+  __shared__ int s_tot[kMaxExperts];
+  __shared__ int s_bef[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
   __shared__ int wh[kWaves * kMaxExperts];
-  const int w = threadIdx.x / kWave;
+  __shared__ int s_wave[kWaves + 1];
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
   const int lane = lane_id();
-  for (int i = threadIdx.x; i < kWaves * n_buckets; i += kBlock) wh[i] = 0;
+  const int me = blockIdx.x;
+  const int per = n_experts / n_segments;
+  const int n_buckets = sorted ? n_experts : n_segments;
+
+  // 1. totals and before-counts per expert
+  for (int e = tid; e < n_experts; e += kBlock) {
+    int tot = 0, bef = 0;
+    int c = 0;
+    for (; c + 8 <= n_chunks; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = hist[int64_t(c + i) * n_experts + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        tot += v[i];
+        bef += (c + i < me) ? v[i] : 0;
+      }
+    }
+    for (; c < n_chunks; ++c) {
+      const int v = hist[int64_t(c) * n_experts + e];
+      tot += v;
+      bef += (c < me) ? v : 0;
+    }
+    s_tot[e] = tot;
+    s_bef[e] = bef;
+  }
+  for (int i = tid; i < kWaves * n_buckets; i += kBlock) wh[i] = 0;
   __syncthreads();
-  const int64_t q0 = int64_t(blockIdx.x) * chunk;
+
+  // 2. exclusive scan of the totals: thread i takes experts [i*kPer, i*kPer + kPer)
+  int local[kPer];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid * kPer + i;
+    local[i] = e < n_experts ? s_tot[e] : 0;
+    sum += local[i];
+  }
+  int total;
+  int run = block_exclusive_scan(sum, s_wave, &total);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid * kPer + i;
+    if (e < n_experts) s_off[e] = run;
+    run += local[i];
+  }
+  if (tid == 0) s_off[n_experts] = total;
+  __syncthreads();
+  if (me == 0) {
+    for (int e = tid; e < n_experts; e += kBlock) {
+      counts[e] = s_tot[e];
+      offsets[e] = s_off[e];
+    }
+    if (tid == 0) offsets[n_experts] = total;
+    for (int g = tid; g <= n_segments; g += kBlock) seg_offsets[g] = s_off[g * per];
+  }
+  if (identity) return;   // the count kernel already wrote the identity maps
+
+  // 3. this chunk's bucket starts (kept in s_tot, no longer needed)
+  if (sorted) {
+    for (int e = tid; e < n_experts; e += kBlock) s_tot[e] = s_off[e] + s_bef[e];
+  } else {
+    for (int g = tid; g < n_segments; g += kBlock) {
+      int b = s_off[g * per];
+      for (int e = g * per; e < (g + 1) * per; ++e) b += s_bef[e];
+      s_tot[g] = b;
+    }
+  }
+
+  // 4. per-wave counts of this chunk, then per-wave starts
+  const int64_t q0 = int64_t(me) * chunk;
   const int64_t q1 = q0 + chunk < nk ? q0 + chunk : nk;
   const int sub = chunk / kWaves;
   const int64_t s0 = q0 + int64_t(w) * sub < q1 ? q0 + int64_t(w) * sub : q1;
   const int64_t s1 = s0 + sub < q1 ? s0 + sub : q1;
   int* mine = wh + w * n_buckets;
-  for (int64_t q = s0 + lane; q < s1; q += kWave) {
-    const int e = idx[q];
-    if (unsigned(e) < unsigned(n_experts)) atomicAdd(&mine[bucket_of(e, sorted, per_segment)], 1);
-  }
+  wave_count(idx, s0, s1, n_experts, sorted, per, mine);
   __syncthreads();
-  const int32_t* bp = base + int64_t(blockIdx.x) * n_buckets;
-  for (int b = threadIdx.x; b < n_buckets; b += kBlock) {
-    int run = bp[b];
+  for (int b = tid; b < n_buckets; b += kBlock) {
+    int r = s_tot[b];
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
       const int c = wh[ww * n_buckets + b];
-      wh[ww * n_buckets + b] = run;
-      run += c;
+      wh[ww * n_buckets + b] = r;
+      r += c;
     }
   }
   __syncthreads();
-  ordered_walk(idx, s0, s1, n_experts, sorted, per_segment, nbits, mine, dst_pos, src_pair,
-               row_expert);
+  ordered_walk(idx, s0, s1, n_experts, sorted, per, nbits, mine, dst_pos, src_pair, row_expert);
 }
 
 // ------------------------------------------------------------------ small problems
@@ -326,7 +389,37 @@ __global__ void zero_offsets_kernel(int n_experts, int n_segments, int32_t* coun
 }
 
 // ------------------------------------------------------------------ row copy
-// One wave per (token, slice) item; each lane moves U vectors of type V.
+// Token rows are read once per dispatch: non-temporal loads for the 16-byte
+// path, plain loads for the narrow fallback types.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_once(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <typename V>
+__device__ __forceinline__ V load_once(const V* p) { return *p; }
+
+// An empty asm statement that reads and writes the value's registers: the
+// compiler must have the value in registers (its load waited for) at this point.
+__device__ __forceinline__ void consume(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+__device__ __forceinline__ void consume(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
+__device__ __forceinline__ void consume(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void consume(uint16_t& v) {
+  uint32_t t = v;
+  asm volatile("" : "+v"(t));
+  v = uint16_t(t);
+}
+__device__ __forceinline__ void consume(uint8_t& v) {
+  uint32_t t = v;
+  asm volatile("" : "+v"(t));
+  v = uint8_t(t);
+}
+
+// One wave per (token, slice) item; each lane moves U vectors of type V.  The
+// loads use clamped (always valid) indices so they issue back to back.  Lane
+// j < k holds destination j (read with readlane).
 template <typename V, int U>
 __global__ __launch_bounds__(kBlock) void scatter_rows_kernel(const V* __restrict__ x,
                                                               int64_t n_tokens, int64_t nvec,
@@ -339,19 +432,28 @@ __global__ __launch_bounds__(kBlock) void scatter_rows_kernel(const V* __restric
   const int64_t t = item / n_slices;
   if (t >= n_tokens) return;
   const int64_t v0 = (item - t * n_slices) * int64_t(kWave * U) + lane;
+  const int my_p = lane < k ? dst_pos[t * k + lane] : -1;
   const V* src = x + t * nvec;
+  // Lanes past the end of the row take index nvec - 1: they load and store the
+  // same value as the lane that owns it, so no store needs a predicate.
   V buf[U];
+  int64_t vi[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (v0 + u * kWave < nvec) buf[u] = src[v0 + u * kWave];
-  const int32_t* dp = dst_pos + t * k;
+  for (int u = 0; u < U; ++u) {
+    vi[u] = v0 + u * kWave < nvec ? v0 + u * kWave : nvec - 1;
+    buf[u] = load_once(src + vi[u]);
+  }
+  // Consume the loaded registers once here so the loads are waited for before
+  // the store loop; otherwise the wait lands inside the loop, where it would
+  // also wait for the previous destination's stores (vmcnt counts both).
+#pragma unroll
+  for (int u = 0; u < U; ++u) consume(buf[u]);
   for (int j = 0; j < k; ++j) {
-    const int p = dp[j];
+    const int p = __builtin_amdgcn_readlane(my_p, j);
     if (unsigned(p) >= uint64_t(nk)) continue;
     V* dst = rows + int64_t(p) * nvec;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (v0 + u * kWave < nvec) dst[v0 + u * kWave] = buf[u];
+    for (int u = 0; u < U; ++u) dst[vi[u]] = buf[u];
   }
 }
 
@@ -446,7 +548,7 @@ DispatchPlan plan_dispatch(int64_t n_tokens, int n_experts, int k, int n_segment
 size_t dispatch_workspace_bytes(int64_t n_tokens, int n_experts, int k, int n_segments) {
   const DispatchPlan p = plan_dispatch(n_tokens, n_experts, k, n_segments);
   const size_t cells = size_t(p.n_chunks > 0 ? p.n_chunks : 1) * size_t(n_experts);
-  return 2 * cells * sizeof(int32_t) + 256;
+  return cells * sizeof(int32_t) + 256;
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
@@ -467,17 +569,14 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
         a.expert_offsets, a.segment_offsets, a.dst_pos, a.src_pair, a.row_expert, a.status);
   } else {
     int32_t* hist = static_cast<int32_t*>(a.workspace);
-    int32_t* base = hist + size_t(p.n_chunks) * a.n_experts;
     count_kernel<<<p.n_chunks, kBlock, 0, stream>>>(a.topk_idx, p.nk, a.n_experts, p.chunk, hist,
                                                     a.status, identity, a.dst_pos, a.src_pair,
                                                     a.row_expert);
-    scan_kernel<<<1, 1024, 0, stream>>>(hist, p.n_chunks, a.n_experts, a.n_segments, a.sorted,
-                                        base, a.expert_counts, a.expert_offsets,
-                                        a.segment_offsets);
-    if (!identity)
-      rank_kernel<<<p.n_chunks, kBlock, 0, stream>>>(a.topk_idx, p.nk, a.n_experts, p.chunk,
-                                                     a.sorted, per, n_buckets, nbits, base,
-                                                     a.dst_pos, a.src_pair, a.row_expert);
+    // identity layout: only block 0's offsets are needed
+    rank_kernel<<<identity ? 1 : p.n_chunks, kBlock, 0, stream>>>(
+        a.topk_idx, p.nk, a.n_experts, a.n_segments, p.chunk, p.n_chunks, a.sorted, identity,
+        nbits, hist, a.expert_counts, a.expert_offsets, a.segment_offsets, a.dst_pos,
+        a.src_pair, a.row_expert);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

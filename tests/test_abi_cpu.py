@@ -137,3 +137,16 @@ def test_dequant_and_swiglu_errors():
     assert g(FAKE, -1, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 30, None) == ARG
     assert g(None, 16, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 30, None) == ARG
     assert g(FAKE, 16, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 16, None) == WS
+
+
+def test_row_copy_errors():
+    s, g = lib.moe_scatter_rows, lib.moe_gather_rows
+    assert s(FAKE, -1, 16, 2, FAKE, FAKE, None) == ARG
+    assert s(FAKE, 4, 0, 2, FAKE, FAKE, None) == ARG
+    assert s(FAKE, 4, 16, 0, FAKE, FAKE, None) == ARG
+    assert s(None, 4, 16, 2, FAKE, FAKE, None) == ARG
+    assert s(FAKE, 2**30, 16, 4, FAKE, FAKE, None) == UNSUP
+    assert s(None, 0, 16, 2, None, None, None) == 0
+    assert g(FAKE, 4, 16, 2, FAKE, -1, FAKE, None) == ARG
+    assert g(FAKE, 4, 16, 2, None, 8, FAKE, None) == ARG
+    assert g(None, 4, 16, 2, None, 0, None, None) == 0

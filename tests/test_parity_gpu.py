@@ -325,3 +325,81 @@ def test_dequant_rows_bit_exact():
     y = moe.moe_dequant_rows(to_dev(rows), to_dev(scales))
     _sync()
     assert np.array_equal(to_np(y), dequant_rows(rows, scales))
+
+
+# ----------------------------------------------------------------- graph capture
+
+def test_path_in_hip_graph_matches_eager_every_replay():
+    """route -> dispatch -> scatter -> combine captured in one graph; every
+    replay (with eager work and syncs in between) equals the eager result."""
+    cfg = CONFIGS["decode"]
+    inp = make_inputs(cfg)
+    logits, x = to_dev(inp["logits"]), to_dev(inp["x"])
+    n, k = cfg.n_tokens, cfg.top_k
+    idx = torch.empty((n, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((n, k), dtype=torch.float32, device=DEV)
+    ws = torch.empty(moe.moe_dispatch_workspace_bytes(n, cfg.n_experts, k, 1), dtype=torch.uint8, device=DEV)
+    res = moe.moe_dispatch(None, idx.zero_(), cfg.n_experts, 1, sort=1, workspace=ws)
+    rows = torch.empty((n * k, cfg.hidden), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((n, cfg.hidden), dtype=torch.bfloat16, device=DEV)
+
+    def step(sort):
+        moe.moe_route_topk(logits, k, topk_idx=idx, topk_w=w)
+        moe.moe_dispatch(None, idx, cfg.n_experts, 1, sort=sort, workspace=ws, out=res)
+        moe.moe_scatter_rows(x, res.dst_pos, k, rows=rows)
+        moe.moe_combine(rows, res.dst_pos, w, out=out)
+
+    for sort in (0, 1):
+        step(sort)
+        _sync()
+        eager = (to_np(out).copy(), to_np(res.dst_pos).copy(), to_np(rows).copy())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(sort)
+        for rep in range(4):
+            out.zero_()
+            rows.zero_()
+            res.dst_pos.fill_(-7)
+            _sync()
+            g.replay()
+            _sync()
+            assert np.array_equal(to_np(out), eager[0]), (sort, rep)
+            assert np.array_equal(to_np(res.dst_pos), eager[1]), (sort, rep)
+            assert np.array_equal(to_np(rows), eager[2]), (sort, rep)
+
+
+# ----------------------------------------------------------------- row copies on their own
+
+@pytest.mark.parametrize("row_elems,np_dtype", [(7168, np.uint16), (40, np.uint16), (3, np.uint16),
+                                                (64, np.float32), (5, np.float32)])
+@pytest.mark.parametrize("sort", [0, 1])
+def test_scatter_and_gather_rows_forms(row_elems, np_dtype, sort):
+    rng = np.random.default_rng(row_elems + sort)
+    n, e, k, g = 300, 64, 8, 4
+    idx = np.stack([rng.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    x = (rng.integers(0, 2**16, (n, row_elems), dtype=np.uint16) if np_dtype == np.uint16
+         else rng.standard_normal((n, row_elems)).astype(np.float32))
+    res = moe.moe_dispatch(None, to_dev(idx), e, g, sort=sort)
+    xd = to_dev(x)
+    rows_s = moe.moe_scatter_rows(xd, res.dst_pos, k)
+    rows_g = moe.moe_gather_rows(xd, res.src_pair, k)
+    _sync()
+    ref = od.dispatch(idx, e, g, bool(sort))
+    expect_g = od.gather_rows(x, ref["src_pair"], k)
+    expect_s = od.scatter_rows(x, ref["dst_pos"], k)
+    assert np.array_equal(expect_g, expect_s)
+    assert np.array_equal(to_np(rows_s).view(np.uint8), expect_s.view(np.uint8))
+    assert np.array_equal(to_np(rows_g).view(np.uint8), expect_g.view(np.uint8))
+
+
+def test_scatter_rows_fp8_scales_as_bytes():
+    cfg = CONFIGS["segment"].with_tokens(100)
+    inp = make_inputs(cfg)
+    idx = np.stack([np.random.default_rng(t).permutation(256)[:8] for t in range(100)]).astype(np.int32)
+    res = moe.moe_dispatch(None, to_dev(idx), 256, 8, sort=0)
+    rows = moe.moe_scatter_rows(to_dev(inp["x"]), res.dst_pos, 8)
+    scales = moe.moe_scatter_rows(to_dev(inp["x_scales"]), res.dst_pos, 8)
+    _sync()
+    ref = od.dispatch(idx, 256, 8, False, x=inp["x"], x_scales=inp["x_scales"])
+    assert np.array_equal(to_np(rows), ref["rows"])
+    assert np.array_equal(to_np(scales), ref["row_scales"])
