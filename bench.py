@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "segment", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a plain device copy of known size (PMC counter calibration)")
@@ -172,6 +173,42 @@ def check_outputs(path):
         raise RuntimeError("combine output of the timed run differs from the oracle")
 
 
+def time_swiglu(torch, moe, steps=10, warmup=2):
+    """The Mixtral-like layer's grouped SwiGLU (N=8192, k=2 -> 16384 rows,
+    D=4096, F=14336, E=8) reading the sorted dispatch in place."""
+    from workloads import CONFIGS, make_inputs, make_swiglu_weights_device
+    cfg = CONFIGS["mixtral"]
+    inp = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    w = make_swiglu_weights_device(cfg)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    idx, tw = moe.moe_route_topk(logits, cfg.top_k)
+    res = moe.moe_dispatch(x, idx, cfg.n_experts, 1, sort=-1, sort_cutoff=cfg.sort_cutoff)
+    rows = res.rows.shape[0]
+    ws = torch.empty(moe.moe_grouped_swiglu_workspace_bytes(rows, cfg.n_experts, cfg.hidden, cfg.ffn),
+                     dtype=torch.uint8, device=dev)
+    y = torch.empty_like(res.rows)
+    call = lambda: moe.moe_grouped_swiglu(res.rows, res.expert_offsets, w["w_gate"], w["w_up"],
+                                          w["w_down"], y=y, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flop = 2.0 * rows * cfg.hidden * cfg.ffn * 3
+    tflops = flop / (ms * 1e-3) / 1e12
+    return {"workload": f"mixtral: {cfg.note}", "rows": rows, "ms": round(ms, 3),
+            "tflops": round(tflops, 1), "peak_tflops": 2500.0, "frac": round(tflops / 2500.0, 4),
+            "flop": flop, "dtype": "bf16 in, fp32 accumulate"}
+
+
 # ------------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(cfg, n_sample, min_seconds=10.0, max_repeats=5):
@@ -295,6 +332,8 @@ def main():
                          "GB_per_s": round(db["total"] / (dms * 1e-3) / 1e9, 1),
                          "cache": "hot (33 MB of buffers stay in the 256 MB last-level cache)",
                          "stages_us": {nm: round(float(v), 2) for nm, v in zip(names, dst_us)}}
+    if not args.no_gemm and args.workload == "prefill":
+        rec["grouped_swiglu"] = time_swiglu(torch, moe)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
     print(json.dumps(rec), flush=True)

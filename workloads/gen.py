@@ -135,6 +135,27 @@ def make_swiglu_weights(cfg: WorkloadConfig, experts=None) -> dict:
     return out
 
 
+def make_swiglu_weights_device(cfg: WorkloadConfig, device="cuda:0") -> dict:
+    """The expert weights of a full-size workload drawn directly in device
+    memory (2.8 GB of bf16 for the Mixtral-like layer would take minutes to
+    draw on the host): torch's seeded Philox generator draws N(0, 1) in
+    float32, scaled by weight_std and rounded to bfloat16 by torch's cast.
+    Returns bfloat16 tensors w_gate, w_up [E, F, D] and w_down [E, D, F]."""
+    if cfg.ffn <= 0:
+        raise ValueError("workload has identity experts")
+    e, f, d = cfg.n_experts, cfg.ffn, cfg.hidden
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg.seed * 1000003 + 17)
+    out = {}
+    for name, shape in (("w_gate", (e, f, d)), ("w_up", (e, f, d)), ("w_down", (e, d, f))):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        for i in range(e):                       # one expert at a time bounds the fp32 temporary
+            t[i] = (torch.randn(shape[1:], generator=gen, device=device, dtype=torch.float32)
+                    * cfg.weight_std).to(torch.bfloat16)
+        out[name] = t
+    return out
+
+
 def alternating_sort(call_index: int) -> int:
     """The segment-major workload toggles the runtime sort flag per call:
     even calls unsorted, odd calls sorted."""
