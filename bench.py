@@ -32,9 +32,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill.json")
-KERNEL_SOURCES = {              # kernel -> source file whose hash must match the counters
-    "scatter": "combine_moe_route_topk_amd/csrc/dispatch.hip",
-    "combine": "combine_moe_route_topk_amd/csrc/combine.hip",
+KERNEL_SOURCES = {              # kernel -> sources whose hash must match the counters' run
+    "scatter": ["combine_moe_route_topk_amd/csrc/dispatch.hip",
+                "combine_moe_route_topk_amd/csrc/device_common.hpp"],
+    "combine": ["combine_moe_route_topk_amd/csrc/combine.hip",
+                "combine_moe_route_topk_amd/csrc/device_common.hpp"],
 }
 
 
@@ -65,9 +67,12 @@ def algorithmic_bytes(n, d, e, k, g, elem):
                 total=route + maps + scatter + combine)
 
 
-def source_sha(rel):
-    with open(os.path.join(ROOT, rel), "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def source_sha(rels):
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 # ------------------------------------------------------------------ GPU side
