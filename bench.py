@@ -78,11 +78,15 @@ def source_sha(rels):
 # ------------------------------------------------------------------ GPU side
 
 class Path:
-    """Preallocated buffers and the four calls of one step."""
+    """Preallocated buffers and the calls of one step.
 
-    def __init__(self, cfg, torch, moe):
+    split=True:  moe_route_dispatch (maps only) | moe_scatter_rows | moe_combine,
+                 so the row-copy kernel can be timed on its own (prefill);
+    split=False: moe_route_dispatch with the payload | moe_combine (decode)."""
+
+    def __init__(self, cfg, torch, moe, split=True):
         from workloads import make_inputs
-        self.torch, self.moe, self.cfg = torch, moe, cfg
+        self.torch, self.moe, self.cfg, self.split = torch, moe, cfg, split
         dev = torch.device("cuda:0")
         inp = make_inputs(cfg)
         self.inputs = inp
@@ -94,41 +98,42 @@ class Path:
             self.x = torch.from_numpy(inp["x"]).to(dev)
         else:
             raise ValueError("bench workloads carry bf16 or fp32 payloads")
-        self.idx = torch.empty((n, k), dtype=torch.int32, device=dev)
-        self.w = torch.empty((n, k), dtype=torch.float32, device=dev)
-        self.rows = torch.empty((n * k, d), dtype=self.x.dtype, device=dev)
         self.out = torch.empty((n, d), dtype=self.x.dtype, device=dev)
-        self.ws = torch.empty(moe.moe_dispatch_workspace_bytes(n, e, k, g), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(moe.moe_route_dispatch_workspace_bytes(n, e, k, g), dtype=torch.uint8,
+                              device=dev)
         self.sort = cfg.sort if cfg.sort in (-1, 0, 1) else 1
-        self.res = moe.moe_dispatch(None, self.idx.zero_(), e, g, sort=self.sort, workspace=self.ws)
+        self.idx, self.w, self.res = moe.moe_route_dispatch(
+            self.logits, None if split else self.x, k, g, cfg.renormalize, self.sort,
+            cfg.sort_cutoff, workspace=self.ws)
+        self.rows = torch.empty((n * k, d), dtype=self.x.dtype, device=dev) if split else self.res.rows
         self.stream = torch.cuda.current_stream()
 
     def step(self, ev=None):
         moe, c = self.moe, self.cfg
         if ev: ev[0].record(self.stream)
-        moe.moe_route_topk(self.logits, c.top_k, c.renormalize, topk_idx=self.idx, topk_w=self.w)
+        moe.moe_route_dispatch(self.logits, None if self.split else self.x, c.top_k, c.n_segments,
+                               c.renormalize, self.sort, c.sort_cutoff, topk_idx=self.idx,
+                               topk_w=self.w, workspace=self.ws, out=self.res)
         if ev: ev[1].record(self.stream)
-        moe.moe_dispatch(None, self.idx, c.n_experts, c.n_segments, sort=self.sort,
-                         sort_cutoff=c.sort_cutoff, workspace=self.ws, out=self.res)
+        if self.split:
+            moe.moe_scatter_rows(self.x, self.res.dst_pos, c.top_k, rows=self.rows)
         if ev: ev[2].record(self.stream)
-        moe.moe_scatter_rows(self.x, self.res.dst_pos, c.top_k, rows=self.rows)
-        if ev: ev[3].record(self.stream)
         moe.moe_combine(self.rows, self.res.dst_pos, self.w, out=self.out)
-        if ev: ev[4].record(self.stream)
+        if ev: ev[3].record(self.stream)
 
 
 def time_path(path, steps, warmup):
     torch = path.torch
     for _ in range(warmup):
         path.step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         path.step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(steps)])
+    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(steps)])
     return wall / steps * 1e3, stage.mean(axis=0) * 1e3, np.median(stage, axis=0) * 1e3
 
 
@@ -284,8 +289,8 @@ def main():
     b = algorithmic_bytes(n, d, e, k, g, cfg.elem_bytes)
     value = b["total"] / (ms * 1e-3) / 1e9
 
-    names = ["route", "maps", "scatter", "combine"]
-    dom = "scatter" if stage_mean_us[2] >= stage_mean_us[3] else "combine"
+    names = ["route+maps", "scatter", "combine"]
+    dom = "scatter" if stage_mean_us[1] >= stage_mean_us[2] else "combine"
     di = names.index(dom)
     achieved = b[dom] / (stage_mean_us[di] * 1e-6) / 1e9
     traffic = None
@@ -325,7 +330,7 @@ def main():
     check_outputs(path)
     if not args.no_decode and args.workload == "prefill":
         dcfg = CONFIGS["decode"]
-        dpath = Path(dcfg, torch, moe)
+        dpath = Path(dcfg, torch, moe, split=False)
         dms, dst_us, _ = time_path(dpath, max(args.steps, 200), args.warmup)
         check_outputs(dpath)
         db = algorithmic_bytes(dcfg.n_tokens, dcfg.hidden, dcfg.n_experts, dcfg.top_k,
@@ -334,9 +339,11 @@ def main():
         check_outputs(dpath)
         rec["decode"] = {"workload": f"decode: {dcfg.note}", "us_per_layer": round(dms * 1e3, 2),
                          "us_per_layer_hipgraph": round(gms * 1e3, 2),
+                         "calls": "moe_route_dispatch (with rows) + moe_combine",
                          "GB_per_s": round(db["total"] / (dms * 1e-3) / 1e9, 1),
                          "cache": "hot (33 MB of buffers stay in the 256 MB last-level cache)",
-                         "stages_us": {nm: round(float(v), 2) for nm, v in zip(names, dst_us)}}
+                         "stages_us": {"route+dispatch": round(float(dst_us[0] + dst_us[1]), 2),
+                                       "combine": round(float(dst_us[2]), 2)}}
     if not args.no_gemm and args.workload == "prefill":
         rec["grouped_swiglu"] = time_swiglu(torch, moe)
     if not args.no_cpu_baseline:

@@ -32,6 +32,10 @@ SIGNATURES = {
     "moe_dispatch": (ctypes.c_int, [_p, _p, _i32, _i64, _i64, _p, _i32, _i32, _i32, _i32, _i32,
                                     ctypes.POINTER(_i32), _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                     _sz, _p]),
+    "moe_route_dispatch_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
+    "moe_route_dispatch": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _i32, _i64, _i64, _i32, _i32, _i32,
+                                          _i32, _i32, ctypes.POINTER(_i32), _p, _p, _p, _p, _p, _p,
+                                          _p, _p, _p, _sz, _p]),
     "moe_scatter_rows": (ctypes.c_int, [_p, _i64, _i64, _i32, _p, _p, _p]),
     "moe_gather_rows": (ctypes.c_int, [_p, _i64, _i64, _i32, _p, _i64, _p, _p]),
     "moe_combine": (ctypes.c_int, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _i32, _p]),

@@ -17,7 +17,8 @@ import torch
 from ._lib import (MOE_BF16, MOE_F32, MOE_F8E4M3, MOE_SORT_AUTO, MoeError, check, lib)
 
 __all__ = ["moe_route_topk", "moe_resolve_sorted", "moe_dispatch_workspace_bytes", "moe_dispatch",
-           "moe_combine", "moe_dequant_rows", "moe_scatter_rows", "moe_gather_rows", "moe_grouped_swiglu_workspace_bytes",
+           "moe_combine", "moe_dequant_rows", "moe_scatter_rows", "moe_gather_rows",
+           "moe_route_dispatch", "moe_route_dispatch_workspace_bytes", "moe_grouped_swiglu_workspace_bytes",
            "moe_grouped_swiglu", "moe_abi_version", "DispatchResult", "MoeError"]
 
 
@@ -139,6 +140,62 @@ def moe_dispatch(x: Optional[torch.Tensor], topk_idx: torch.Tensor, n_experts: i
         workspace.numel(), _stream(stream)))
     out.sorted = bool(used.value)
     return out
+
+
+def moe_route_dispatch_workspace_bytes(n_tokens: int, n_experts: int, k: int,
+                                       n_segments: int = 1) -> int:
+    return int(lib.moe_route_dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments))
+
+
+def moe_route_dispatch(logits: torch.Tensor, x: Optional[torch.Tensor], k: int,
+                       n_segments: int = 1, renormalize: bool = True, sort: int = MOE_SORT_AUTO,
+                       sort_cutoff: int = 256, x_scales: Optional[torch.Tensor] = None,
+                       topk_idx: Optional[torch.Tensor] = None,
+                       topk_w: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       out: Optional[DispatchResult] = None, want_row_expert: bool = True,
+                       stream=None):
+    """Routing and dispatch in one call -> (topk_idx, topk_w, DispatchResult)."""
+    _need(logits, "logits", (torch.float32,))
+    dev = logits.device
+    n, e = logits.shape
+    nk = n * k
+    if topk_idx is None:
+        topk_idx = torch.empty((n, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((n, k), dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", (torch.int32,), dev)
+    _need(topk_w, "topk_w", (torch.float32,), dev)
+    if x is not None:
+        _need(x, "x", tuple(_PAYLOAD), dev)
+        if x.shape[0] != n:
+            raise ValueError("x and logits disagree on N")
+        dtype, hidden = _PAYLOAD[x.dtype], x.shape[1]
+    else:
+        dtype, hidden = MOE_BF16, 1
+    if x_scales is not None:
+        _need(x_scales, "x_scales", (torch.float32,), dev)
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        rows = None if x is None else torch.empty((nk, hidden), dtype=x.dtype, device=dev)
+        rs = None if x_scales is None else torch.empty((nk, x_scales.shape[1]), dtype=torch.float32, device=dev)
+        out = DispatchResult(False, torch.empty(e, **i32), torch.empty(e + 1, **i32),
+                             torch.empty(n_segments + 1, **i32), torch.empty(nk, **i32),
+                             torch.empty(nk, **i32),
+                             torch.empty(nk, **i32) if want_row_expert else None, rows, rs)
+    if workspace is None:
+        wsb = moe_route_dispatch_workspace_bytes(n, e, k, n_segments)
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), dev)
+    used = ctypes.c_int32(-1)
+    check("moe_route_dispatch", lib.moe_route_dispatch(
+        _ptr(logits), int(bool(renormalize)), _ptr(topk_idx), _ptr(topk_w), _ptr(x), _ptr(x_scales),
+        dtype, n, hidden, e, k, n_segments, sort, sort_cutoff, ctypes.byref(used), _ptr(out.rows),
+        _ptr(out.row_scales), _ptr(out.expert_counts), _ptr(out.expert_offsets),
+        _ptr(out.segment_offsets), _ptr(out.src_pair), _ptr(out.dst_pos), _ptr(out.row_expert),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    out.sorted = bool(used.value)
+    return topk_idx, topk_w, out
 
 
 def moe_scatter_rows(x: torch.Tensor, dst_pos: torch.Tensor, k: int,

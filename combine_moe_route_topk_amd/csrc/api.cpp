@@ -99,13 +99,19 @@ size_t moe_dispatch_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t
   return moe::dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments);
 }
 
-int moe_dispatch(const void* x, const float* x_scales, int32_t dtype, int64_t n_tokens,
-                 int64_t hidden, const int32_t* topk_idx, int32_t n_experts, int32_t k,
-                 int32_t n_segments, int32_t sort, int32_t sort_cutoff, int32_t* sorted_used,
-                 void* rows, float* row_scales, int32_t* expert_counts, int32_t* expert_offsets,
-                 int32_t* segment_offsets, int32_t* src_pair, int32_t* dst_pos,
-                 int32_t* row_expert, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "moe_dispatch";
+}  // extern "C"
+
+namespace {
+
+// Shared argument checking and packing of moe_dispatch / moe_route_dispatch.
+// Returns MOE_OK and fills `a` (and `sorted`) or returns the error status.
+int prepare_dispatch(const char* fn, const void* x, const float* x_scales, int32_t dtype,
+                     int64_t n_tokens, int64_t hidden, const int32_t* topk_idx, int32_t n_experts,
+                     int32_t k, int32_t n_segments, int32_t sort, int32_t sort_cutoff, void* rows,
+                     float* row_scales, int32_t* expert_counts, int32_t* expert_offsets,
+                     int32_t* segment_offsets, int32_t* src_pair, int32_t* dst_pos,
+                     int32_t* row_expert, void* workspace, size_t workspace_bytes, size_t need,
+                     moe::DispatchArgs& a) {
   int rc = check_routing_sizes(fn, n_tokens, n_experts, k);
   if (rc) return rc;
   if (hidden < 1) return fail(MOE_ERR_ARG, "%s: hidden < 1", fn);
@@ -136,15 +142,12 @@ int moe_dispatch(const void* x, const float* x_scales, int32_t dtype, int64_t n_
   int32_t sorted = 0;
   rc = resolve_sorted(sort, n_tokens, sort_cutoff, &sorted);
   if (rc) return rc;
-  const size_t need = moe::dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments);
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace ? workspace_bytes : size_t(0));
   if (reinterpret_cast<uintptr_t>(workspace) & 15)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
-  if (sorted_used) *sorted_used = sorted;
-
-  moe::DispatchArgs a{};
+  a = moe::DispatchArgs{};
   a.x = x;
   a.x_scales = x_scales;
   a.row_bytes = hidden * elem;
@@ -164,24 +167,88 @@ int moe_dispatch(const void* x, const float* x_scales, int32_t dtype, int64_t n_
   a.dst_pos = dst_pos;
   a.row_expert = row_expert;
   a.workspace = workspace;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool validate = validate_mode();
-  int32_t* status = nullptr;
-  if (validate) {
-    // the status word sits in the last 16 bytes of the workspace region
-    status = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + need - 16);
-    hipError_t e = hipMemsetAsync(status, 0, sizeof(int32_t), s);
-    if (e != hipSuccess) return hip_status(e, fn);
-  }
-  a.status = status;
-  rc = hip_status(moe::launch_dispatch(a, s), fn);
-  if (rc || !validate) return rc;
+  return MOE_OK;
+}
+
+// Validate mode: clear the status word before the launches, then wait and
+// report out-of-range expert ids.
+int32_t* validate_begin(void* workspace, size_t need, hipStream_t s, int* rc, const char* fn) {
+  int32_t* status = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + need - 16);
+  hipError_t e = hipMemsetAsync(status, 0, sizeof(int32_t), s);
+  *rc = e == hipSuccess ? MOE_OK : hip_status(e, fn);
+  return status;
+}
+
+int validate_end(int32_t* status, hipStream_t s, int32_t n_experts, const char* fn) {
   int32_t host_status = 0;
   hipError_t e = hipMemcpyAsync(&host_status, status, sizeof(int32_t), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_status(e, fn);
   if (host_status) return fail(MOE_ERR_ARG, "%s: topk_idx holds expert ids outside [0, %d)", fn, n_experts);
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_dispatch(const void* x, const float* x_scales, int32_t dtype, int64_t n_tokens,
+                 int64_t hidden, const int32_t* topk_idx, int32_t n_experts, int32_t k,
+                 int32_t n_segments, int32_t sort, int32_t sort_cutoff, int32_t* sorted_used,
+                 void* rows, float* row_scales, int32_t* expert_counts, int32_t* expert_offsets,
+                 int32_t* segment_offsets, int32_t* src_pair, int32_t* dst_pos,
+                 int32_t* row_expert, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_dispatch";
+  const int early = check_routing_sizes(fn, n_tokens, n_experts, k);
+  if (early) return early;
+  const size_t need = moe::dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments > 0 ? n_segments : 1);
+  moe::DispatchArgs a;
+  int rc = prepare_dispatch(fn, x, x_scales, dtype, n_tokens, hidden, topk_idx, n_experts, k,
+                            n_segments, sort, sort_cutoff, rows, row_scales, expert_counts,
+                            expert_offsets, segment_offsets, src_pair, dst_pos, row_expert,
+                            workspace, workspace_bytes, need, a);
+  if (rc) return rc;
+  if (sorted_used) *sorted_used = a.sorted;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool validate = validate_mode();
+  if (validate) {
+    a.status = validate_begin(workspace, need, s, &rc, fn);
+    if (rc) return rc;
+  }
+  rc = hip_status(moe::launch_dispatch(a, s), fn);
+  if (rc || !validate) return rc;
+  return validate_end(a.status, s, n_experts, fn);
+}
+
+size_t moe_route_dispatch_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t k,
+                                          int32_t n_segments) {
+  if (moe_dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments) == 0) return 0;
+  return moe::route_dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments);
+}
+
+int moe_route_dispatch(const float* logits, int32_t renormalize, int32_t* topk_idx, float* topk_w,
+                       const void* x, const float* x_scales, int32_t dtype, int64_t n_tokens,
+                       int64_t hidden, int32_t n_experts, int32_t k, int32_t n_segments,
+                       int32_t sort, int32_t sort_cutoff, int32_t* sorted_used, void* rows,
+                       float* row_scales, int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* segment_offsets, int32_t* src_pair, int32_t* dst_pos,
+                       int32_t* row_expert, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  const char* fn = "moe_route_dispatch";
+  const int early = check_routing_sizes(fn, n_tokens, n_experts, k);
+  if (early) return early;
+  if (n_tokens > 0 && (!logits || !topk_idx || !topk_w))
+    return fail(MOE_ERR_ARG, "%s: null routing pointer", fn);
+  const size_t need = moe::route_dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments > 0 ? n_segments : 1);
+  moe::DispatchArgs a;
+  int rc = prepare_dispatch(fn, x, x_scales, dtype, n_tokens, hidden, topk_idx, n_experts, k,
+                            n_segments, sort, sort_cutoff, rows, row_scales, expert_counts,
+                            expert_offsets, segment_offsets, src_pair, dst_pos, row_expert,
+                            workspace, workspace_bytes, need, a);
+  if (rc) return rc;
+  if (sorted_used) *sorted_used = a.sorted;
+  moe::RouteArgs r{logits, renormalize ? 1 : 0, topk_w};
+  return hip_status(moe::launch_route_dispatch(r, a, static_cast<hipStream_t>(stream)), fn);
 }
 
 int moe_scatter_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int32_t k,

@@ -224,6 +224,16 @@ __global__ __launch_bounds__(kBlock) void rank_kernel(const int32_t* __restrict_
   for (int e = tid; e < n_experts; e += kBlock) {
     int tot = 0, bef = 0;
     int c = 0;
+    for (; c + 32 <= n_chunks; c += 32) {          // 32 loads in flight per thread
+      int v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = hist[int64_t(c + i) * n_experts + e];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        tot += v[i];
+        bef += (c + i < me) ? v[i] : 0;
+      }
+    }
     for (; c + 8 <= n_chunks; c += 8) {
       int v[8];
 #pragma unroll
@@ -288,7 +298,7 @@ __global__ __launch_bounds__(kBlock) void rank_kernel(const int32_t* __restrict_
   // 4. per-wave counts of this chunk, then per-wave starts
   const int64_t q0 = int64_t(me) * chunk;
   const int64_t q1 = q0 + chunk < nk ? q0 + chunk : nk;
-  const int sub = chunk / kWaves;
+  const int sub = (chunk + kWaves - 1) / kWaves;
   const int64_t s0 = q0 + int64_t(w) * sub < q1 ? q0 + int64_t(w) * sub : q1;
   const int64_t s1 = s0 + sub < q1 ? s0 + sub : q1;
   int* mine = wh + w * n_buckets;
@@ -589,6 +599,19 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
                          a.row_scales, stream);
   }
   return err;
+}
+
+size_t route_dispatch_workspace_bytes(int64_t n_tokens, int n_experts, int k, int n_segments) {
+  return dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments);
+}
+
+hipError_t launch_route_dispatch(const RouteArgs& r, const DispatchArgs& a, hipStream_t stream) {
+  if (a.n_tokens > 0) {
+    hipError_t err = launch_route_topk(r.logits, a.n_tokens, a.n_experts, a.k, r.renormalize,
+                                       const_cast<int32_t*>(a.topk_idx), r.topk_w, stream);
+    if (err != hipSuccess) return err;
+  }
+  return launch_dispatch(a, stream);
 }
 
 hipError_t launch_scatter_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int k,

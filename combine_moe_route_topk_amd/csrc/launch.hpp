@@ -48,6 +48,15 @@ struct DispatchArgs {
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
+// Routing followed by dispatch on the same stream.
+struct RouteArgs {
+  const float* logits;
+  int renormalize;
+  float* topk_w;
+};
+size_t route_dispatch_workspace_bytes(int64_t n_tokens, int n_experts, int k, int n_segments);
+hipError_t launch_route_dispatch(const RouteArgs& r, const DispatchArgs& a, hipStream_t stream);
+
 // Row copies on their own (byte payloads): scatter form rows[dst_pos[q]] =
 // x[q / k] and gather form rows[p] = x[src_pair[p] / k].
 hipError_t launch_scatter_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int k,

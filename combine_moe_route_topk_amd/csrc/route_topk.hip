@@ -61,27 +61,28 @@ __device__ __forceinline__ int wave_min_i32(int v) {
   return v;
 }
 
+// Loads one token's logits: lane l holds experts l + 64 r.
 template <int R>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
-                                                         int64_t n_tokens, int n_experts, int k,
-                                                         int renormalize,
-                                                         int32_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_w) {
+__device__ __forceinline__ void load_token(const float* __restrict__ row, int n_experts,
+                                           float (&val)[R]) {
   const int lane = lane_id();
-  const int64_t t = int64_t(blockIdx.x) * (blockDim.x / kWave) +
-                    __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
-  if (t >= n_tokens) return;                          // uniform per wave
-  const float* row = logits + t * n_experts;
-
-  uint32_t ov[R];
-  float val[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int e = lane + r * kWave;
-    const bool in = e < n_experts;
-    val[r] = in ? row[e] : 0.f;
-    ov[r] = in ? ordered_bits(val[r]) : 0u;           // 0 is below every real value
+    val[r] = e < n_experts ? row[e] : 0.f;
   }
+}
+
+// Routes one token with the calling wave from its loaded logits: returns, in
+// lane j < k, the expert of slot j and its weight.
+template <int R>
+__device__ __forceinline__ void select_token(const float (&val)[R], int n_experts, int k,
+                                             int renormalize, int& out_e, float& out_w) {
+  const int lane = lane_id();
+  uint32_t ov[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    ov[r] = lane + r * kWave < n_experts ? ordered_bits(val[r]) : 0u;   // 0: below every value
   auto local_best = [&](uint32_t& bo, int& br) {
     bo = ov[0];
     br = 0;
@@ -129,9 +130,28 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
       if (lane + r * kWave < n_experts) s += expf(val[r] - top);
     den = wave_reduce_sum(s);
   }
+  out_e = my_e;
+  out_w = num / den;
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int64_t n_tokens, int n_experts, int k,
+                                                         int renormalize,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w) {
+  const int lane = lane_id();
+  const int64_t t = int64_t(blockIdx.x) * (blockDim.x / kWave) +
+                    __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
+  if (t >= n_tokens) return;                          // uniform per wave
+  float val[R];
+  load_token<R>(logits + t * n_experts, n_experts, val);
+  int e;
+  float w;
+  select_token<R>(val, n_experts, k, renormalize, e, w);
   if (lane < k) {
-    topk_idx[t * k + lane] = my_e;
-    topk_w[t * k + lane] = num / den;
+    topk_idx[t * k + lane] = e;
+    topk_w[t * k + lane] = w;
   }
 }
 

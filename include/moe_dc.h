@@ -179,6 +179,28 @@ int moe_dispatch(const void* x, const float* x_scales, int32_t dtype,
                  int32_t* src_pair, int32_t* dst_pos, int32_t* row_expert,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- route + dispatch
+ * moe_route_dispatch_workspace_bytes -- workspace of moe_route_dispatch
+ * (at least moe_dispatch_workspace_bytes for the same sizes).  0 for invalid
+ * sizes. */
+size_t moe_route_dispatch_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t k,
+                                          int32_t n_segments);
+
+/* moe_route_dispatch -- moe_route_topk followed by moe_dispatch in one call,
+ * with the same outputs as the two calls made in sequence (bit for bit).
+ *   logits [N, E] f32, renormalize, topk_idx [N, k] i32 (output, then read
+ *   by the dispatch), topk_w [N, k] f32 (output); every other argument as in
+ *   moe_dispatch; workspace of moe_route_dispatch_workspace_bytes(N, E, k, G).
+ * Errors: those of moe_route_topk and moe_dispatch. */
+int moe_route_dispatch(const float* logits, int32_t renormalize, int32_t* topk_idx, float* topk_w,
+                       const void* x, const float* x_scales, int32_t dtype, int64_t n_tokens,
+                       int64_t hidden, int32_t n_experts, int32_t k, int32_t n_segments,
+                       int32_t sort, int32_t sort_cutoff, int32_t* sorted_used, void* rows,
+                       float* row_scales, int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* segment_offsets, int32_t* src_pair, int32_t* dst_pos,
+                       int32_t* row_expert, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* moe_scatter_rows -- the row copy of moe_dispatch on its own, scatter form
  * (packet_scatter / dispatch_local of [MLX-EP]):
  *   rows[dst_pos[t*k + j]] = x[t]   for every token t and slot j,

@@ -150,3 +150,28 @@ def test_row_copy_errors():
     assert g(FAKE, 4, 16, 2, FAKE, -1, FAKE, None) == ARG
     assert g(FAKE, 4, 16, 2, None, 8, FAKE, None) == ARG
     assert g(None, 4, 16, 2, None, 0, None, None) == 0
+
+
+def test_route_dispatch_errors():
+    f = lib.moe_route_dispatch
+
+    def call(**kw):
+        a = dict(logits=FAKE, renorm=1, idx=FAKE, w=FAKE, x=FAKE, xs=None, dtype=1, n=4, d=64, e=8,
+                 k=2, g=1, sort=1, cutoff=256, used=None, rows=FAKE, rs=None, counts=FAKE, offs=FAKE,
+                 segs=FAKE, src=FAKE, dst=FAKE, rexp=FAKE, ws=FAKE, wsb=1 << 20)
+        a.update(kw)
+        return f(a["logits"], a["renorm"], a["idx"], a["w"], a["x"], a["xs"], a["dtype"], a["n"],
+                 a["d"], a["e"], a["k"], a["g"], a["sort"], a["cutoff"], a["used"], a["rows"], a["rs"],
+                 a["counts"], a["offs"], a["segs"], a["src"], a["dst"], a["rexp"], a["ws"], a["wsb"], None)
+
+    assert call(logits=None) == ARG
+    assert call(w=None) == ARG
+    assert call(k=9) == ARG
+    assert call(g=3) == ARG
+    assert call(rows=None) == ARG
+    assert call(ws=None) == WS
+    assert call(wsb=8) == WS
+    assert call(e=2048) == UNSUP
+    g = lib.moe_route_dispatch_workspace_bytes
+    assert g(4096, 256, 8, 1) >= lib.moe_dispatch_workspace_bytes(4096, 256, 8, 1)
+    assert g(4, 8, 9, 1) == 0
