@@ -128,10 +128,12 @@ __device__ __forceinline__ void ordered_walk(const int32_t* __restrict__ idx, in
   }
 }
 
-// Per-wave bucket counts of pairs [s0, s1) into cnt[] (LDS atomics: counts do
-// not depend on order).
+// Per-wave counts of pairs [s0, s1) into cnt[] by bucket (if cnt) and exp[] by
+// expert (if exp), with LDS atomics (counts do not depend on order); out-of-
+// range ids set *bad.  Ids are fetched four steps ahead.
 __device__ __forceinline__ void wave_count(const int32_t* __restrict__ idx, int64_t s0, int64_t s1,
-                                           int n_experts, int sorted, int per_segment, int* cnt) {
+                                           int n_experts, int sorted, int per_segment, int* cnt,
+                                           int* exp, bool* bad) {
   constexpr int kAhead = 4;
   const int lane = lane_id();
   for (int64_t qa = s0; qa < s1; qa += kAhead * kWave) {
@@ -142,8 +144,17 @@ __device__ __forceinline__ void wave_count(const int32_t* __restrict__ idx, int6
       ev[i] = q < s1 ? idx[q] : -1;
     }
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i)
-      if (unsigned(ev[i]) < unsigned(n_experts)) atomicAdd(&cnt[bucket_of(ev[i], sorted, per_segment)], 1);
+    for (int i = 0; i < kAhead; ++i) {
+      const int64_t q = qa + i * kWave + lane;
+      if (q >= s1) continue;
+      const int e = ev[i];
+      if (unsigned(e) < unsigned(n_experts)) {
+        if (cnt) atomicAdd(&cnt[bucket_of(e, sorted, per_segment)], 1);
+        if (exp) atomicAdd(&exp[e], 1);
+      } else if (bad) {
+        *bad = true;
+      }
+    }
   }
 }
 
@@ -302,7 +313,7 @@ __global__ __launch_bounds__(kBlock) void rank_kernel(const int32_t* __restrict_
   const int64_t s0 = q0 + int64_t(w) * sub < q1 ? q0 + int64_t(w) * sub : q1;
   const int64_t s1 = s0 + sub < q1 ? s0 + sub : q1;
   int* mine = wh + w * n_buckets;
-  wave_count(idx, s0, s1, n_experts, sorted, per, mine);
+  wave_count(idx, s0, s1, n_experts, sorted, per, mine, nullptr, nullptr);
   __syncthreads();
   for (int b = tid; b < n_buckets; b += kBlock) {
     int r = s_tot[b];
@@ -320,8 +331,8 @@ __global__ __launch_bounds__(kBlock) void rank_kernel(const int32_t* __restrict_
 // ------------------------------------------------------------------ small problems
 __global__ __launch_bounds__(kSmallThreads) void small_meta_kernel(
     const int32_t* __restrict__ idx, int64_t nk, int n_experts, int n_segments, int sorted,
-    int nbits, int identity, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ seg_offsets, int32_t* __restrict__ dst_pos,
+    int nbits, int identity, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ seg_offsets, int32_t* __restrict__ dst_pos,
     int32_t* __restrict__ src_pair, int32_t* __restrict__ row_expert, int32_t* status) {
   __shared__ int h[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
@@ -343,20 +354,14 @@ __global__ __launch_bounds__(kSmallThreads) void small_meta_kernel(
   const int64_t s1 = s0 + sub < nk ? s0 + sub : nk;
   int* mine = wh + w * n_buckets;
   bool bad = false;
-  for (int64_t q = s0 + lane; q < s1; q += kWave) {
-    const int e = idx[q];
-    if (unsigned(e) < unsigned(n_experts)) {
-      atomicAdd(&h[e], 1);
-      if (!identity) atomicAdd(&mine[bucket_of(e, sorted, per)], 1);
-    } else {
-      bad = true;
-    }
-    if (identity) {
+  if (identity) {
+    for (int64_t q = s0 + lane; q < s1; q += kWave) {
       dst_pos[q] = int32_t(q);
       src_pair[q] = int32_t(q);
-      if (row_expert) row_expert[q] = e;
+      if (row_expert) row_expert[q] = idx[q];
     }
   }
+  wave_count(idx, s0, s1, n_experts, sorted, per, identity ? nullptr : mine, h, &bad);
   if (bad && status) atomicOr(status, 1);
   __syncthreads();
 
