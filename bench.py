@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-all", action="store_true", help="skip the five-workload table")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a plain device copy of known size (PMC counter calibration)")
@@ -190,6 +191,78 @@ def check_outputs(path):
     got = path.out[torch.from_numpy(toks).to(path.out.device)].float().cpu().numpy()
     if not np.all(np.abs(got - exact) <= 2.0 ** -7 * np.abs(exact) + 1e-30):
         raise RuntimeError("combine output of the timed run differs from the oracle")
+
+
+def dc_bytes(cfg):
+    """Algorithmic bytes of route + dispatch + combine for any workload (fp8
+    payloads move one byte per element plus their fp32 block scales; the
+    combine reads bf16 expert outputs)."""
+    n, d, e, k, g = cfg.n_tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.n_segments
+    nk = n * k
+    b = algorithmic_bytes(n, d, e, k, g, cfg.elem_bytes)
+    if cfg.dtype == "f8":
+        sc = d // 128 * 4
+        b["scatter"] += (n + nk) * sc
+        b["combine"] = nk * d * 2 + 2 * nk * 4 + n * d * 2
+        b["total"] = b["route"] + b["maps"] + b["scatter"] + b["combine"]
+    return b
+
+
+def time_all_configs(torch, moe, steps, warmup):
+    """route -> dispatch (maps and rows) -> combine for each of the five
+    workloads, captured in a HIP graph and replayed.  Expert outputs are an
+    input of the combine: identity experts read the dispatched rows; the fp8
+    workload's identity expert (dequantisation to bf16) runs once before the
+    timing.  The segment-major workload alternates the sort flag per call, so
+    its step is two calls (unsorted, then sorted) and the figure is per call."""
+    from workloads import CONFIGS, make_inputs
+    dev = torch.device("cuda:0")
+    out = {}
+    for name, cfg in CONFIGS.items():
+        inp = make_inputs(cfg)
+        logits = torch.from_numpy(inp["logits"]).to(dev)
+        if cfg.dtype == "bf16":
+            x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        elif cfg.dtype == "f32":
+            x = torch.from_numpy(inp["x"]).to(dev)
+        else:
+            x = torch.from_numpy(inp["x"]).to(dev)
+        xs = torch.from_numpy(inp["x_scales"]).to(dev) if inp["x_scales"] is not None else None
+        n, k, e, g = cfg.n_tokens, cfg.top_k, cfg.n_experts, cfg.n_segments
+        sorts = [0, 1] if cfg.sort == "alternate" else [cfg.sort]
+        ws = torch.empty(moe.moe_route_dispatch_workspace_bytes(n, e, k, g), dtype=torch.uint8, device=dev)
+        idx, w, res = moe.moe_route_dispatch(logits, x, k, g, cfg.renormalize, sorts[0], cfg.sort_cutoff,
+                                             x_scales=xs, workspace=ws)
+        y = moe.moe_dequant_rows(res.rows, res.row_scales) if cfg.dtype == "f8" else res.rows
+        o = torch.empty((n, cfg.hidden), dtype=y.dtype, device=dev)
+
+        def step():
+            for srt in sorts:
+                moe.moe_route_dispatch(logits, x, k, g, cfg.renormalize, srt, cfg.sort_cutoff,
+                                       x_scales=xs, topk_idx=idx, topk_w=w, workspace=ws, out=res)
+                moe.moe_combine(y, res.dst_pos, w, out=o)
+
+        step()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        for _ in range(warmup):
+            gr.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        reps = max(steps, 50)
+        for _ in range(reps):
+            gr.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / reps / len(sorts) * 1e6
+        b = dc_bytes(cfg)["total"]
+        out[name] = {"us_per_layer": round(us, 2), "GB_per_s": round(b / (us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes": b, "mode": "alternating unsorted/sorted" if len(sorts) > 1 else
+                     ("sorted" if res.sorted else "unsorted")}
+        del x, xs, y, o, res, ws, logits
+    return out
 
 
 def time_swiglu(torch, moe, steps=10, warmup=2):
@@ -356,6 +429,8 @@ def main():
                          "cache": "hot (33 MB of buffers stay in the 256 MB last-level cache)",
                          "stages_us": {"route+dispatch": round(float(dst_us[0] + dst_us[1]), 2),
                                        "combine": round(float(dst_us[2]), 2)}}
+    if not args.no_all and args.workload == "prefill":
+        rec["all_configs"] = time_all_configs(torch, moe, args.steps, args.warmup)
     if not args.no_gemm and args.workload == "prefill":
         rec["grouped_swiglu"] = time_swiglu(torch, moe)
     if not args.no_cpu_baseline:

@@ -22,7 +22,7 @@
 //             Multisplit", PPoPP 2016);
 //   copy   -- scatter form: one wave reads a slice of token t's row once and
 //             writes it to the k destination rows dst_pos[t*k + j].
-// Small problems (NK <= 16384, at most 256 buckets) run count, scan and rank
+// Small problems (NK <= 4096, at most 256 buckets) run count, scan and rank
 // in one workgroup.  Nothing is read back to the host: NK rows is always the
 // output size.
 #include "device_common.hpp"
@@ -35,7 +35,7 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / kWave;
-constexpr int64_t kSmallMaxPairs = 16384;
+constexpr int64_t kSmallMaxPairs = 4096;
 constexpr int kSmallMaxBuckets = 256;
 
 __device__ __forceinline__ int bucket_of(int e, int sorted, int per_segment) {

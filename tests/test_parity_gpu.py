@@ -110,9 +110,9 @@ def test_dispatch_full_size(name):
 
 
 @pytest.mark.parametrize("n,e,k,g", [
-    (1, 8, 2, 1), (3, 8, 8, 2), (129, 16, 4, 4), (2047, 256, 8, 8),     # one-workgroup path
-    (3000, 64, 8, 4), (2049, 32, 8, 1), (100, 512, 4, 8),               # multi-block path
-    (300, 1024, 8, 1024), (5000, 1024, 1, 16), (64, 1000, 32, 8),
+    (1, 8, 2, 1), (3, 8, 8, 2), (129, 16, 4, 4), (512, 256, 8, 8),      # one-workgroup path (NK <= 4096)
+    (513, 256, 8, 8), (2047, 256, 8, 8), (3000, 64, 8, 4), (2049, 32, 8, 1),   # multi-block path
+    (100, 512, 4, 8), (300, 1024, 8, 1024), (5000, 1024, 1, 16), (64, 1000, 32, 8),
 ])
 @pytest.mark.parametrize("sort", [0, 1])
 def test_dispatch_shapes(n, e, k, g, sort):
