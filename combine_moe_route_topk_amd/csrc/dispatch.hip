@@ -472,6 +472,52 @@ __global__ __launch_bounds__(kBlock) void scatter_rows_kernel(const V* __restric
   }
 }
 
+// Payload rows and their block-scale rows in one launch (fp8 workloads):
+// items [0, items_a) copy payload slices, the rest copy scale rows; both with
+// 16-byte accesses.
+template <int U>
+__global__ __launch_bounds__(kBlock) void scatter_pair_kernel(
+    const uint4* __restrict__ xa, int64_t nvec_a, int n_slices_a, uint4* __restrict__ rows_a,
+    const uint4* __restrict__ xb, int64_t nvec_b, int n_slices_b, uint4* __restrict__ rows_b,
+    int64_t n_tokens, int k, const int32_t* __restrict__ dst_pos, int64_t nk) {
+  const int lane = lane_id();
+  int64_t item = __builtin_amdgcn_readfirstlane(int(blockIdx.x)) * int64_t(kBlock / kWave) +
+                 __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
+  const int64_t items_a = n_tokens * n_slices_a;
+  const uint4* x = xa;
+  uint4* rows = rows_a;
+  int64_t nvec = nvec_a;
+  int n_slices = n_slices_a;
+  if (item >= items_a) {
+    item -= items_a;
+    x = xb;
+    rows = rows_b;
+    nvec = nvec_b;
+    n_slices = n_slices_b;
+  }
+  const int64_t t = item / n_slices;
+  if (t >= n_tokens) return;
+  const int64_t v0 = (item - t * n_slices) * int64_t(kWave * U) + lane;
+  const int my_p = lane < k ? dst_pos[t * k + lane] : -1;
+  const uint4* src = x + t * nvec;
+  uint4 buf[U];
+  int64_t vi[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    vi[u] = v0 + u * kWave < nvec ? v0 + u * kWave : nvec - 1;
+    buf[u] = load_once(src + vi[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) consume(buf[u]);
+  for (int j = 0; j < k; ++j) {
+    const int p = __builtin_amdgcn_readlane(my_p, j);
+    if (unsigned(p) >= uint64_t(nk)) continue;
+    uint4* dst = rows + int64_t(p) * nvec;
+#pragma unroll
+    for (int u = 0; u < U; ++u) dst[vi[u]] = buf[u];
+  }
+}
+
 template <typename V>
 hipError_t launch_scatter_typed(const void* x, int64_t n_tokens, int64_t row_bytes, int k,
                                 const int32_t* dst_pos, int64_t nk, void* rows,
@@ -595,6 +641,25 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (a.x && a.x_scales) {
+    const uint64_t align = uint64_t(a.row_bytes) | uint64_t(a.scale_bytes) |
+                           reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.rows) |
+                           reinterpret_cast<uintptr_t>(a.x_scales) |
+                           reinterpret_cast<uintptr_t>(a.row_scales);
+    if ((align & 15) == 0) {      // payload and scales in one launch
+      constexpr int U = 2;
+      const int64_t nva = a.row_bytes / 16, nvb = a.scale_bytes / 16;
+      const int nsa = int((nva + kWave * U - 1) / (kWave * U));
+      const int nsb = int((nvb + kWave * U - 1) / (kWave * U));
+      const int64_t items = a.n_tokens * (nsa + nsb);
+      const int per_block = kBlock / kWave;
+      scatter_pair_kernel<U><<<unsigned((items + per_block - 1) / per_block), kBlock, 0, stream>>>(
+          static_cast<const uint4*>(a.x), nva, nsa, static_cast<uint4*>(a.rows),
+          reinterpret_cast<const uint4*>(a.x_scales), nvb, nsb, reinterpret_cast<uint4*>(a.row_scales),
+          a.n_tokens, a.k, a.dst_pos, p.nk);
+      return hipGetLastError();
+    }
+  }
   if (a.x) {
     err = launch_scatter(a.x, a.n_tokens, a.row_bytes, a.k, a.dst_pos, p.nk, a.rows, stream);
     if (err != hipSuccess) return err;
