@@ -332,6 +332,11 @@ int moe_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
   if (n_rows == 0) return ok();
   if (!rows || !expert_offsets || !w_gate || !w_up || !w_down || !y)
     return fail(MOE_ERR_ARG, "%s: null pointer argument", fn);
+  // the operands are read in 16-byte runs straight into LDS
+  if ((reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(w_gate) |
+       reinterpret_cast<uintptr_t>(w_up) | reinterpret_cast<uintptr_t>(w_down) |
+       reinterpret_cast<uintptr_t>(y)) & 15)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: rows, weights and y must be 16-byte aligned", fn);
   const size_t need = moe::grouped_swiglu_workspace_bytes(n_rows, n_experts, hidden, ffn);
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,

@@ -278,8 +278,9 @@ size_t moe_grouped_swiglu_workspace_bytes(int64_t n_rows, int32_t n_experts, int
  *   w_gate, w_up    [E, F, D] bfloat16;  w_down [E, D, F] bfloat16
  *   y               [n_rows, D] bfloat16, output, same row order as rows
  * Errors: MOE_ERR_ARG for null pointers (unless n_rows == 0), sizes < 1;
- * MOE_ERR_UNSUPPORTED for D % 64 != 0, F % 64 != 0 or E > MOE_MAX_EXPERTS;
- * MOE_ERR_WORKSPACE for a short workspace. */
+ * MOE_ERR_UNSUPPORTED for D % 64 != 0, F % 64 != 0, E > MOE_MAX_EXPERTS, or
+ * rows, a weight tensor or y not 16-byte aligned;
+ * MOE_ERR_WORKSPACE for a short workspace or one not 256-byte aligned. */
 int moe_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                        const int32_t* expert_offsets, int32_t n_experts,
                        const void* w_gate, const void* w_up, const void* w_down, int64_t ffn,

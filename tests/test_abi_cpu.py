@@ -137,6 +137,11 @@ def test_dequant_and_swiglu_errors():
     assert g(FAKE, -1, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 30, None) == ARG
     assert g(None, 16, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 30, None) == ARG
     assert g(FAKE, 16, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 16, None) == WS
+    odd = ctypes.c_void_p(0x1008)    # 8-byte aligned only: the operands are read in 16-byte runs
+    assert g(odd, 16, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 30, None) == UNSUP
+    assert g(FAKE, 16, 64, FAKE, 8, FAKE, FAKE, odd, 128, FAKE, FAKE, 1 << 30, None) == UNSUP
+    assert g(FAKE, 16, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, odd, FAKE, 1 << 30, None) == UNSUP
+    assert b"16-byte" in lib.moe_last_error()
 
 
 def test_row_copy_errors():
