@@ -157,3 +157,36 @@ def test_swiglu_pins_catch_sigmoid_for_silu(monkeypatch):
     monkeypatch.setattr(tsw, "silu", osw.silu)
     _fails(tsw.test_silu_closed_forms)
     _fails(tsw.test_rows_match_pure_python_brute_force)
+
+
+# ------------------------------------------------------------------ fp8 grouped GEMM mutants
+
+from oracle import gemm_fp8 as og
+from tests import test_oracle_gemm_fp8 as tg
+
+
+def _product_mutant(kind):
+    def f(xq, sx, wq_e, sw_e, absolute=False):
+        m, k = xq.shape
+        nb = k // og.BLOCK
+        out = np.zeros((m, wq_e.shape[0]))
+        for b in range(nb - 1 if kind == "drop_last_block" else nb):
+            cols = slice(b * og.BLOCK, (b + 1) * og.BLOCK)
+            partial = xq[:, cols] @ wq_e[:, cols].T
+            if kind == "transposed_weight_scales":
+                col_scale = np.resize(sw_e.T.ravel(), sw_e.size).reshape(sw_e.shape)[:, b]
+            else:
+                col_scale = sw_e[:, b]
+            row_scale = sx[:, (b + 1) % nb] if kind == "row_scale_next_block" else sx[:, b]
+            scale = np.repeat(col_scale.astype(np.float64), og.BLOCK)[None, :] * \
+                row_scale.astype(np.float64)[:, None]
+            out += scale * partial
+        return out
+    return f
+
+
+@pytest.mark.parametrize("kind", ["transposed_weight_scales", "row_scale_next_block",
+                                  "drop_last_block"])
+def test_fp8_gemm_pins_catch(monkeypatch, kind):
+    monkeypatch.setattr(og, "_expert_product", _product_mutant(kind))
+    _fails(tg.test_closed_form_constant_codes_non_square_block_grid)
