@@ -291,3 +291,31 @@ def moe_grouped_swiglu(rows: torch.Tensor, expert_offsets: torch.Tensor, w_gate:
         _ptr(rows), r, d, _ptr(expert_offsets), e, _ptr(w_gate), _ptr(w_up), _ptr(w_down), f,
         _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
+
+
+def moe_grouped_gemm_fp8(rows: torch.Tensor, row_scales: torch.Tensor, expert_offsets: torch.Tensor,
+                         w: torch.Tensor, w_scales: torch.Tensor, y: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """rows [R, K] E4M3FN codes (uint8) with row_scales [R, K/128] f32, grouped
+    by expert through expert_offsets [E+1]; w [E, N, K] E4M3FN codes with
+    w_scales [E, N/128, K/128] f32 -> y [R, N] bf16."""
+    _need(rows, "rows", (torch.uint8,))
+    dev = rows.device
+    _need(row_scales, "row_scales", (torch.float32,), dev)
+    _need(expert_offsets, "expert_offsets", (torch.int32,), dev)
+    _need(w, "w", (torch.uint8,), dev)
+    _need(w_scales, "w_scales", (torch.float32,), dev)
+    r, k = rows.shape
+    e, n, k2 = w.shape
+    if k2 != k or tuple(row_scales.shape) != (r, k // 128) or \
+            tuple(w_scales.shape) != (e, n // 128, k // 128) or expert_offsets.numel() != e + 1:
+        raise ValueError("moe_grouped_gemm_fp8: inconsistent shapes")
+    if y is None:
+        y = torch.empty((r, n), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", (torch.bfloat16,), dev)
+    if tuple(y.shape) != (r, n):
+        raise ValueError("moe_grouped_gemm_fp8: y must be [R, N]")
+    check("moe_grouped_gemm_fp8", lib.moe_grouped_gemm_fp8(
+        _ptr(rows), _ptr(row_scales), r, k, _ptr(expert_offsets), e, _ptr(w), _ptr(w_scales), n,
+        _ptr(y), _stream(stream)))
+    return y

@@ -349,4 +349,35 @@ int moe_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                     fn);
 }
 
+int moe_grouped_gemm_fp8(const void* rows, const float* row_scales, int64_t n_rows,
+                         int64_t k_dim, const int32_t* expert_offsets, int32_t n_experts,
+                         const void* w, const float* w_scales, int64_t n_dim, void* y,
+                         void* stream) {
+  const char* fn = "moe_grouped_gemm_fp8";
+  if (n_rows < 0) return fail(MOE_ERR_ARG, "%s: n_rows < 0", fn);
+  if (k_dim < 1 || n_dim < 1 || n_experts < 1) return fail(MOE_ERR_ARG, "%s: sizes must be >= 1", fn);
+  if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "%s: n_experts > %d", fn, MOE_MAX_EXPERTS);
+  if (k_dim % 128 != 0 || n_dim % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: k_dim and n_dim must be multiples of 128", fn);
+  if (k_dim > int64_t(moe::kMaxFp8Blocks) * 128)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: k_dim > %d", fn, moe::kMaxFp8Blocks * 128);
+  if (n_rows > INT32_MAX || n_dim > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: sizes exceed the int32 range", fn);
+  const int64_t tiles = ((n_rows + 63) / 64 + n_experts) * (n_dim / 128);
+  if (tiles > INT32_MAX - 8) return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  if (n_rows == 0) return ok();
+  if (!rows || !row_scales || !expert_offsets || !w || !w_scales || !y)
+    return fail(MOE_ERR_ARG, "%s: null pointer argument", fn);
+  // operands are read in 16-byte runs; scales as 4-byte words
+  if ((reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(w) |
+       reinterpret_cast<uintptr_t>(y)) & 15)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: rows, w and y must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(row_scales) | reinterpret_cast<uintptr_t>(w_scales)) & 3)
+    return fail(MOE_ERR_ARG, "%s: scales must be 4-byte aligned", fn);
+  return hip_status(moe::launch_grouped_gemm_fp8(rows, row_scales, n_rows, k_dim, expert_offsets,
+                                                 n_experts, w, w_scales, n_dim, y,
+                                                 static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

@@ -286,6 +286,34 @@ int moe_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                        const void* w_gate, const void* w_up, const void* w_down, int64_t ffn,
                        void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_grouped_gemm_fp8 -- fp8 block-scaled grouped expert GEMM reading the
+ * dispatched fp8 rows in place ([1SIDED]: the dispatch is agnostic to the
+ * activation quantisation format, and grouped GEMMs read the received buffers
+ * in place).  Rows are the fp8 dispatch's output: E4M3FN codes with one
+ * float32 scale per 128 elements of a row, grouped by expert.  For expert e and
+ * every row p in [expert_offsets[e], expert_offsets[e+1]):
+ *   y[p, n] = bf16( sum_b row_scales[p, b] * w_scales[e, n/128, b]
+ *                   * sum_{k in block b} q(rows[p, k]) * q(w[e, n, k]) )
+ * with b over the K/128 blocks of 128 and q() the E4M3FN value.  fp8 products
+ * on the matrix cores, fp32 per-block partial sums scaled and accumulated in
+ * fp32, one rounding to bf16.
+ *
+ *   rows            [n_rows, K] E4M3FN codes (uint8), 16-byte aligned
+ *   row_scales      [n_rows, K/128] float32
+ *   expert_offsets  [E+1] int32, device-resident; rows outside
+ *                   [offsets[0], offsets[E]) are neither read nor written
+ *   w               [E, N, K] E4M3FN codes, 16-byte aligned
+ *   w_scales        [E, N/128, K/128] float32
+ *   y               [n_rows, N] bfloat16, output, same row order as rows,
+ *                   16-byte aligned
+ * No workspace.  Errors: MOE_ERR_ARG for null pointers (unless n_rows == 0),
+ * sizes < 1, misaligned scales; MOE_ERR_UNSUPPORTED for K % 128 != 0,
+ * N % 128 != 0, K > 16384, E > MOE_MAX_EXPERTS or misaligned rows / w / y. */
+int moe_grouped_gemm_fp8(const void* rows, const float* row_scales, int64_t n_rows,
+                         int64_t k_dim, const int32_t* expert_offsets, int32_t n_experts,
+                         const void* w, const float* w_scales, int64_t n_dim, void* y,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

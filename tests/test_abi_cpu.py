@@ -19,7 +19,7 @@ FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: every call below fails
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -180,3 +180,23 @@ def test_route_dispatch_errors():
     g = lib.moe_route_dispatch_workspace_bytes
     assert g(4096, 256, 8, 1) >= lib.moe_dispatch_workspace_bytes(4096, 256, 8, 1)
     assert g(4, 8, 9, 1) == 0
+
+
+def test_grouped_gemm_fp8_errors():
+    g = lib.moe_grouped_gemm_fp8     # rows, row_scales, R, K, offsets, E, w, w_scales, N, y, stream
+    assert g(FAKE, FAKE, -1, 128, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == ARG
+    assert g(FAKE, FAKE, 8, 0, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == ARG
+    assert g(FAKE, FAKE, 8, 128, FAKE, 0, FAKE, FAKE, 128, FAKE, None) == ARG
+    assert g(FAKE, FAKE, 8, 100, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == UNSUP      # K % 128
+    assert g(FAKE, FAKE, 8, 128, FAKE, 4, FAKE, FAKE, 200, FAKE, None) == UNSUP      # N % 128
+    assert g(FAKE, FAKE, 8, 128 * 129, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == UNSUP  # K > 16384
+    assert g(FAKE, FAKE, 8, 128, FAKE, 2000, FAKE, FAKE, 128, FAKE, None) == UNSUP   # E
+    assert g(None, FAKE, 8, 128, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == ARG
+    assert g(FAKE, FAKE, 8, 128, FAKE, 4, FAKE, None, 128, FAKE, None) == ARG
+    assert g(None, None, 0, 128, None, 4, None, None, 128, None, None) == 0           # no rows
+    odd = ctypes.c_void_p(0x1008)
+    assert g(odd, FAKE, 8, 128, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == UNSUP
+    assert g(FAKE, FAKE, 8, 128, FAKE, 4, odd, FAKE, 128, FAKE, None) == UNSUP
+    assert g(FAKE, FAKE, 8, 128, FAKE, 4, FAKE, FAKE, 128, odd, None) == UNSUP
+    assert g(FAKE, ctypes.c_void_p(0x1002), 8, 128, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == ARG
+    assert b"aligned" in lib.moe_last_error()

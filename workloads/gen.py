@@ -156,6 +156,37 @@ def make_swiglu_weights_device(cfg: WorkloadConfig, device="cuda:0") -> dict:
     return out
 
 
+# fp8 expert projection consuming the segment-major rows: a DeepSeek-V3-sized
+# expert's gate and up projections (F = 2048 each) stacked, N = 4096, K = 7168.
+FP8_GEMM_N = 4096
+
+
+def make_fp8_expert_weights_device(cfg: WorkloadConfig, n_out: int = FP8_GEMM_N,
+                                   device="cuda:0", weight_std: float = 0.02) -> dict:
+    """fp8 expert weights for a workload, drawn in device memory (256 experts
+    x 4096 x 7168 is 7.5 GB): torch's seeded Philox draws N(0, weight_std) in
+    float32 per expert; each 128 x 128 block gets the scale amax / 448 (1 for
+    an all-zero block) and its codes are torch's round-to-nearest-even cast of
+    w / scale to float8 E4M3FN.  Returns w [E, N, K] uint8 codes and w_scales
+    [E, N/128, K/128] float32."""
+    e, k = cfg.n_experts, cfg.hidden
+    if k % 128 or n_out % 128:
+        raise ValueError("N and K must be multiples of 128")
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg.seed * 1000003 + 29)
+    w = torch.empty((e, n_out, k), dtype=torch.uint8, device=device)
+    ws = torch.empty((e, n_out // 128, k // 128), dtype=torch.float32, device=device)
+    for i in range(e):
+        f = torch.randn((n_out, k), generator=gen, device=device, dtype=torch.float32) * weight_std
+        blocks = f.view(n_out // 128, 128, k // 128, 128)
+        amax = blocks.abs().amax(dim=(1, 3))
+        s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (blocks / s[:, None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        w[i] = q.view(torch.uint8).view(n_out, k)
+        ws[i] = s
+    return {"w": w, "w_scales": ws}
+
+
 def alternating_sort(call_index: int) -> int:
     """The segment-major workload toggles the runtime sort flag per call:
     even calls unsorted, odd calls sorted."""
