@@ -301,6 +301,52 @@ def time_swiglu(torch, moe, steps=10, warmup=2):
             "flop": flop, "dtype": "bf16 in, fp32 accumulate"}
 
 
+def time_fp8_gemm(torch, moe, steps=10, warmup=2):
+    """The segment-major workload's fp8 expert projection (N_out = 4096, K =
+    7168, 256 experts): the sorted fp8 dispatch's rows and 1x128 scales read in
+    place by the block-scaled grouped GEMM.  Weight streaming dominates."""
+    from workloads import CONFIGS, FP8_GEMM_N, make_fp8_expert_weights_device, make_inputs
+    cfg = CONFIGS["segment"]
+    inp = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inp["x"]).to(dev)
+    xs = torch.from_numpy(inp["x_scales"]).to(dev)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    _, _, res = moe.moe_route_dispatch(logits, x, cfg.top_k, cfg.n_segments, cfg.renormalize, 1,
+                                       cfg.sort_cutoff, x_scales=xs)
+    wt = make_fp8_expert_weights_device(cfg)
+    rows = res.rows.shape[0]
+    n, k, e = FP8_GEMM_N, cfg.hidden, cfg.n_experts
+    y = torch.empty((rows, n), dtype=torch.bfloat16, device=dev)
+    call = lambda: moe.moe_grouped_gemm_fp8(res.rows, res.row_scales, res.expert_offsets, wt["w"],
+                                            wt["w_scales"], y=y)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    counts = res.expert_counts.cpu().numpy()
+    active = int((counts > 0).sum())
+    wbytes = active * (n * k + (n // 128) * (k // 128) * 4)
+    b = wbytes + rows * (k + (k // 128) * 4) + rows * n * 2 + (e + 1) * 4
+    gbs = b / (ms * 1e-3) / 1e9
+    flop = 2.0 * rows * n * k
+    out = {"workload": f"segment: {cfg.note}; fp8 projection N={n} read in place", "rows": rows,
+           "active_experts": active, "ms": round(ms, 3), "bytes": b, "weight_bytes": wbytes,
+           "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "tflops": round(flop / (ms * 1e-3) / 1e12, 1), "flop": flop,
+           "bound": "hbm (weights)", "dtype": "fp8 e4m3fn in, fp32 accumulate, bf16 out"}
+    del wt, y, res, x, xs
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(cfg, n_sample, min_seconds=10.0, max_repeats=5):
@@ -433,6 +479,8 @@ def main():
         rec["all_configs"] = time_all_configs(torch, moe, args.steps, args.warmup)
     if not args.no_gemm and args.workload == "prefill":
         rec["grouped_swiglu"] = time_swiglu(torch, moe)
+        torch.cuda.empty_cache()
+        rec["grouped_gemm_fp8"] = time_fp8_gemm(torch, moe)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
     print(json.dumps(rec), flush=True)

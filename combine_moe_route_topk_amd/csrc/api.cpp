@@ -359,9 +359,7 @@ int moe_grouped_gemm_fp8(const void* rows, const float* row_scales, int64_t n_ro
   if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "%s: n_experts > %d", fn, MOE_MAX_EXPERTS);
   if (k_dim % 128 != 0 || n_dim % 128 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "%s: k_dim and n_dim must be multiples of 128", fn);
-  if (k_dim > int64_t(moe::kMaxFp8Blocks) * 128)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: k_dim > %d", fn, moe::kMaxFp8Blocks * 128);
-  if (n_rows > INT32_MAX || n_dim > INT32_MAX)
+  if (n_rows > INT32_MAX || n_dim > INT32_MAX || k_dim > INT32_MAX)
     return fail(MOE_ERR_UNSUPPORTED, "%s: sizes exceed the int32 range", fn);
   const int64_t tiles = ((n_rows + 63) / 64 + n_experts) * (n_dim / 128);
   if (tiles > INT32_MAX - 8) return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", fn);

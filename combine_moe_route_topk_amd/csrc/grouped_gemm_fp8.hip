@@ -14,20 +14,20 @@
 // With ~32 rows per expert (1024 tokens, top-8 over 256 experts) each weight
 // byte feeds ~64 FLOP: the kernel streams weights from HBM, so it is shaped
 // for that rather than for matrix-core peak.
-//   * a tile is 64 rows x 128 columns of one expert; its 4 waves each own 32
-//     columns and both 32-row halves, and run independently (no LDS operand
-//     staging, no barrier in the K loop);
-//   * operands go from global memory straight into registers in the
-//     v_mfma_f32_32x32x16_fp8_fp8 layout: lane l holds row / column l % 32 and
-//     64 contiguous bytes of each 128-wide K block (half l / 32), so every
-//     weight row is read as whole 128-byte lines.  The eight MFMAs of a block
-//     take 8-byte groups g of those 64 bytes, which permutes K identically on
-//     both operands;
+//   * a tile is 64 rows x 128 columns of one expert and K advances in blocks
+//     of 128 (one scale block); its 8 waves each own 32 rows x 32 columns;
+//   * weights and rows go from global memory straight into LDS
+//     (global_load_lds_dwordx4), eight lanes per 128-byte line, so every load
+//     instruction reads whole lines; the row tile is loaded once per
+//     workgroup for its eight waves; each wave's 32 row scales ride along;
+//   * a ring of three LDS slots keeps block kt+2 loading while block kt is
+//     multiplied; one barrier per block publishes block kt+1 and retires the
+//     reads of the slot block kt+2 overwrites.  Two workgroups fit per CU;
+//   * each lane multiplies 64 contiguous bytes of its row and column per
+//     block, 8-byte group g feeding MFMA g (v_mfma_f32_32x32x16_fp8_fp8),
+//     which permutes K identically on both operands;
 //   * each block's fp32 partial sum is scaled by sx * sw and added to the
-//     accumulator; the row scales of the tile are staged once in LDS,
-//     transposed, so a lane's four consecutive rows are one 16-byte read;
-//   * the next block's operands are loaded while the current block is
-//     multiplied (two register sets);
+//     accumulator;
 //   * tiles run column-fastest: the workgroups one XCD runs together share an
 //     expert's rows from L2 while each streams its own weight slab.
 #include "device_common.hpp"
@@ -43,7 +43,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kQB = 128;        // scale block (both operands)
 constexpr int kTM = 64;         // rows per tile
 constexpr int kTN = 128;        // columns per tile
-constexpr int kThreads = 256;   // 4 waves x 32 columns
+constexpr int kThreads = 512;   // 8 waves: 2 row halves x 4 column groups of 32
 constexpr int kXcds = 8;
 constexpr int kLoads = 4;       // 16-byte loads per operand row half per block
 
@@ -94,60 +94,131 @@ __device__ Fp8Tile find_fp8_tile(int m_idx, const int32_t* __restrict__ offs, in
   return t;
 }
 
-// 8-byte operand group g (0..7) of a lane's 64 bytes.
-__device__ __forceinline__ long group8(const u32x4 (&v)[kLoads], int g) {
-  const u32x4 q = v[g >> 1];
-  const unsigned lo = (g & 1) ? q.z : q.x, hi = (g & 1) ? q.w : q.y;
-  return long((unsigned long)lo | ((unsigned long)hi << 32));
+// LDS ring slot: the weight tile (128 columns x 128 bytes of K), the row tile
+// (64 rows x 128 bytes) and, per wave, the scales of its 32 rows for one K
+// block.  Rows of both
+// tiles are 128 bytes with their 16-byte chunks XOR-swizzled by
+// ((row >> 1) & 7): the 16 rows one 16-lane phase of a ds_read_b128 reads
+// fall in 16 distinct 16-byte bank groups.
+constexpr int kWaves = kThreads / 64;
+constexpr int kSlotW = 0;
+constexpr int kSlotA = kTN * kQB;                 // 16 KB
+constexpr int kSlotS = kSlotA + kTM * kQB;        // + 8 KB
+constexpr int kSlotBytes = kSlotS + kWaves * 256; // + each wave's copy of its 32 row scales
+constexpr int kDmaW = kTN * kQB / (kThreads * 16);   // 1 KB runs per wave: weights (2)
+constexpr int kDmaA = kTM * kQB / (kThreads * 16);   // rows (1)
+constexpr int kDmaPerStage = kDmaW + kDmaA + 1;      // + one run of row scales
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kQB + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-struct Stage {
-  u32x4 b[kLoads];    // weight column l % 32
-  u32x4 a0[kLoads];   // row l % 32 of the tile
-  u32x4 a1[kLoads];   // row 32 + l % 32
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): at most n vector-memory operations of this wave
+// outstanding and (lgkm0) all of its LDS operations returned.
+constexpr unsigned wait_vm_lgkm0(int n) {
+  return unsigned(n & 15) | (unsigned((n >> 4) & 3) << 14) | (0x7u << 4);
+}
+constexpr unsigned wait_vm(int n) {
+  return unsigned(n & 15) | (unsigned((n >> 4) & 3) << 14) | (0x7u << 4) | (0xFu << 8);
+}
+
+struct Sources {
+  const uint8_t* w[kDmaW];     // this lane's 16 bytes of each weight run (K block 0)
+  const uint8_t* a[kDmaA];     // and of each row run
+  const float* sx;             // the row scale of K block 0 this lane copies
+  int w_lds[kDmaW], a_lds[kDmaA], s_lds;   // wave-uniform LDS offsets in a slot
 };
 
-__device__ __forceinline__ void load_stage(Stage& s, const uint8_t* wb, const uint8_t* xa0,
-                                           const uint8_t* xa1, int blk) {
+// One direct global->LDS load: M0 holds the LDS byte address of the run and
+// lane l's bytes land at M0 + l * size.  Issued from asm so that the
+// compiler's own wait insertion does not track it (it would conservatively
+// wait for every direct load in flight before reading any ring slot); the
+// explicit vmcnt waits at the block barriers are what orders these loads.
+// The instruction writes no register.
+typedef const __attribute__((address_space(3))) unsigned char* lds_cptr;
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return uint32_t(size_t((lds_cptr)p));
+}
+__device__ __forceinline__ void dma16(const uint8_t* g, const unsigned char* l) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_addr(l)), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const float* g, const unsigned char* l) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds_addr(l)), "v"(g) : "memory", "m0");
+}
+
+// Direct global->LDS loads of K block `blk` into one ring slot (kDmaPerStage
+// operations per wave, every lane active).
+__device__ __forceinline__ void load_block(unsigned char* slot, const Sources& src, int blk) {
   const int64_t o = int64_t(blk) * kQB;
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    s.b[i] = *reinterpret_cast<const u32x4*>(wb + o + 16 * i);
-    s.a0[i] = *reinterpret_cast<const u32x4*>(xa0 + o + 16 * i);
-    s.a1[i] = *reinterpret_cast<const u32x4*>(xa1 + o + 16 * i);
+  for (int i = 0; i < kDmaW; ++i) dma16(src.w[i] + o, slot + src.w_lds[i]);
+#pragma unroll
+  for (int i = 0; i < kDmaA; ++i) dma16(src.a[i] + o, slot + src.a_lds[i]);
+  dma4(src.sx + blk, slot + src.s_lds);
+}
+
+template <unsigned kWait>
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWait);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ long lo8(u32x4 q) {
+  return long((unsigned long)q.x | ((unsigned long)q.y << 32));
+}
+__device__ __forceinline__ long hi8(u32x4 q) {
+  return long((unsigned long)q.z | ((unsigned long)q.w << 32));
+}
+
+// acc += sx * sw * (K block partial products) for this wave's 32 rows and 32
+// columns.  Lane l multiplies bytes [64 * (l / 32), +64) of its row and
+// column; 8-byte group g feeds MFMA g, the same on both operands.
+__device__ __forceinline__ void block_mma(f32x16& acc, const unsigned char* slot, int w_row,
+                                          int a_row, int s_off, int half, float sw) {
+  u32x4 wb[4], a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wb[i] = *reinterpret_cast<const u32x4*>(slot + kSlotW + swz(w_row, half * 4 + i));
+    a[i] = *reinterpret_cast<const u32x4*>(slot + kSlotA + swz(a_row, half * 4 + i));
+  }
+  f32x16 p;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) p[v] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(lo8(a[i]), lo8(wb[i]), p, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(hi8(a[i]), hi8(wb[i]), p, 0, 0, 0);
+  }
+  // lane holds rows 8*(v/4) + 4*half + v%4 of the wave's 32 rows
+  // (read as an ext-vector type like the operands: the compiler then knows the
+  // read cannot touch the slot being loaded and adds no wait for the loads)
+  const unsigned char* sx = slot + s_off + 16 * half;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 s4 = *reinterpret_cast<const u32x4*>(sx + 32 * q);
+    const float r[4] = {__uint_as_float(s4.x), __uint_as_float(s4.y), __uint_as_float(s4.z),
+                        __uint_as_float(s4.w)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[4 * q + i] = __builtin_fmaf(r[i] * sw, p[4 * q + i], acc[4 * q + i]);
   }
 }
 
-// acc += (sx * sw) * (the block's exact-order fp32 partial products)
-__device__ __forceinline__ void block_step(f32x16& acc0, f32x16& acc1, const Stage& s,
-                                           const float* __restrict__ sxt, int blk, float sw,
-                                           int half) {
-  f32x16 p0, p1;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    p0[v] = 0.f;
-    p1[v] = 0.f;
-  }
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const long bg = group8(s.b, g);
-    p0 = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(group8(s.a0, g), bg, p0, 0, 0, 0);
-    p1 = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(group8(s.a1, g), bg, p1, 0, 0, 0);
-  }
-  // lane holds rows 8*(v/4) + 4*half + v%4 of each 32-row half
-  const float* col = sxt + blk * kTM + 4 * half;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 s0 = *reinterpret_cast<const float4*>(col + 8 * q);
-    const float4 s1 = *reinterpret_cast<const float4*>(col + 32 + 8 * q);
-    const float r0[4] = {s0.x, s0.y, s0.z, s0.w};
-    const float r1[4] = {s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc0[4 * q + i] = __builtin_fmaf(r0[i] * sw, p0[4 * q + i], acc0[4 * q + i]);
-      acc1[4 * q + i] = __builtin_fmaf(r1[i] * sw, p1[4 * q + i], acc1[4 * q + i]);
-    }
-  }
+// One K block: wait for block kt (only block kt+1's loads may be in flight),
+// then load block kt+2 into the slot block kt-1 used (every wave has passed
+// this barrier, so all its reads of that slot are done), then multiply.
+__device__ __forceinline__ void block_step(f32x16& acc, const unsigned char* cur, unsigned char* dst,
+                                           const Sources& src, int kt, int kb,
+                                           const float* __restrict__ swp, int w_row, int a_row,
+                                           int s_off, int half) {
+  block_barrier<wait_vm_lgkm0(kDmaPerStage)>();
+  // past the last block the loads repeat it into a slot that is not multiplied
+  load_block(dst, src, min(kt + 2, kb - 1));
+  block_mma(acc, cur, w_row, a_row, s_off, half, swp[kt]);
 }
 
 __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_kernel(
@@ -155,61 +226,89 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_kernel(
     int K, const int32_t* __restrict__ offs, int n_experts, const uint8_t* __restrict__ w,
     const float* __restrict__ w_scales, int N, uint16_t* __restrict__ y, int max_m_tiles,
     int n_tiles) {
-  // row scales of the tile, transposed: sxt[b * 64 + r]
-  __shared__ __align__(16) float sxt[kMaxFp8Blocks * kTM];
+  // three ring slots in distinct arrays, so the compiler can tell the slot
+  // being loaded from the slot being read and adds no wait between them
+  __shared__ __align__(1024) unsigned char slot0[kSlotBytes];
+  __shared__ __align__(1024) unsigned char slot1[kSlotBytes];
+  __shared__ __align__(1024) unsigned char slot2[kSlotBytes];
 
   const int nb = gridDim.x;                 // a multiple of kXcds
   const int b = blockIdx.x;
   const int tile = (b % kXcds) * (nb / kXcds) + b / kXcds;
   if (int64_t(tile) >= int64_t(max_m_tiles) * n_tiles) return;
   const int m_idx = tile / n_tiles, n_tile = tile % n_tiles;
-  const Fp8Tile ti = find_fp8_tile(m_idx, offs, n_experts, n_rows);
+  Fp8Tile ti = find_fp8_tile(m_idx, offs, n_experts, n_rows);
   if (!ti.valid) return;
-
-  const int kb = K / kQB;
-  for (int i = threadIdx.x; i < kb * kTM; i += kThreads) {
-    const int r = i % kTM, blk = i / kTM;
-    int64_t gr = ti.row0 + r;
-    if (gr >= ti.row_end) gr = ti.row_end - 1;   // clamped rows are never stored
-    sxt[blk * kTM + r] = row_scales[gr * kb + blk];
-  }
-  __syncthreads();
+  // the lookup's results are wave-uniform; saying so keeps the tile's
+  // addresses (and the weight-scale loads) in scalar registers
+  ti.expert = __builtin_amdgcn_readfirstlane(ti.expert);
+  ti.row0 = __builtin_amdgcn_readfirstlane(int(ti.row0));
+  ti.row_end = __builtin_amdgcn_readfirstlane(int(ti.row_end));
 
   const int lane = lane_id();
-  const int w_id = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  const int hw = wv >> 2, cg = wv & 3;      // row half and column group of this wave
   const int half = lane >> 5;
-  const int64_t col = int64_t(n_tile) * kTN + w_id * 32 + (lane & 31);
-  int64_t r0 = ti.row0 + (lane & 31), r1 = r0 + 32;
-  if (r0 >= ti.row_end) r0 = ti.row_end - 1;
-  if (r1 >= ti.row_end) r1 = ti.row_end - 1;
-  const uint8_t* wb = w + (int64_t(ti.expert) * N + col) * K + half * 64;
-  const uint8_t* xa0 = rows + r0 * K + half * 64;
-  const uint8_t* xa1 = rows + r1 * K + half * 64;
+  const int kb = K / kQB;
+  const int64_t col0 = int64_t(n_tile) * kTN;
+
+  // Direct-load assignment: run i of wave wv covers 8 rows of a tile (1 KB);
+  // lane l writes LDS bytes l * 16 of the run, i.e. row l / 8, physical chunk
+  // l % 8, which holds logical chunk (l % 8) ^ ((row >> 1) & 7).
+  Sources src;
+#pragma unroll
+  for (int i = 0; i < kDmaW; ++i) {
+    const int run = i * kWaves + wv;
+    const int row = run * 8 + lane / 8;
+    const int c = (lane % 8) ^ ((row >> 1) & 7);
+    src.w[i] = w + (int64_t(ti.expert) * N + col0 + row) * K + c * 16;
+    src.w_lds[i] = kSlotW + run * 1024;
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaA; ++i) {
+    const int run = i * kWaves + wv;
+    const int row = run * 8 + lane / 8;
+    const int c = (lane % 8) ^ ((row >> 1) & 7);
+    int64_t gr = ti.row0 + row;
+    if (gr >= ti.row_end) gr = ti.row_end - 1;       // clamped rows are never stored
+    src.a[i] = rows + gr * K + c * 16;
+    src.a_lds[i] = kSlotA + run * 1024;
+  }
+  {
+    // lane l copies the scale of the wave's row l % 32 (lanes 32..63 repeat it)
+    int64_t gr = ti.row0 + hw * 32 + (lane & 31);
+    if (gr >= ti.row_end) gr = ti.row_end - 1;
+    src.sx = row_scales + gr * kb;
+    src.s_lds = kSlotS + wv * 256;
+  }
   const float* swp = w_scales + (int64_t(ti.expert) * (N / kQB) + n_tile) * kb;
+  const int w_row = cg * 32 + (lane & 31);     // this wave's 32 weight columns
+  const int a_row = hw * 32 + (lane & 31);     // and 32 rows
+  const int s_off = src.s_lds;
 
-  f32x16 acc0, acc1;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  load_block(slot0, src, 0);
+  load_block(slot1, src, min(1, kb - 1));
+  int kt = 0;
+  for (; kt + 3 <= kb; kt += 3) {
+    block_step(acc, slot0, slot2, src, kt, kb, swp, w_row, a_row, s_off, half);
+    block_step(acc, slot1, slot0, src, kt + 1, kb, swp, w_row, a_row, s_off, half);
+    block_step(acc, slot2, slot1, src, kt + 2, kb, swp, w_row, a_row, s_off, half);
+  }
+  if (kt < kb)           // kb % 3 >= 1
+    block_step(acc, slot0, slot2, src, kt, kb, swp, w_row, a_row, s_off, half);
+  if (kt + 1 < kb)       // kb % 3 == 2
+    block_step(acc, slot1, slot0, src, kt + 1, kb, swp, w_row, a_row, s_off, half);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));   // no direct load may outlive the workgroup
+
+  // acc[v] = C[8*(v/4) + 4*half + v%4][lane % 32] of the wave's 32 x 32 block
+  const int64_t col = col0 + cg * 32 + (lane & 31);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    acc0[v] = 0.f;
-    acc1[v] = 0.f;
-  }
-  Stage s0, s1;
-  load_stage(s0, wb, xa0, xa1, 0);
-  for (int blk = 0; blk < kb; blk += 2) {
-    // past the last block the loads repeat it; the result is not used
-    load_stage(s1, wb, xa0, xa1, min(blk + 1, kb - 1));
-    block_step(acc0, acc1, s0, sxt, blk, swp[blk], half);
-    load_stage(s0, wb, xa0, xa1, min(blk + 2, kb - 1));
-    if (blk + 1 < kb) block_step(acc0, acc1, s1, sxt, blk + 1, swp[blk + 1], half);
-  }
-
-  // acc[v] = C[8*(v/4) + 4*half + v%4][lane % 32] of each 32-row half
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int rr = 8 * (v >> 2) + 4 * half + (v & 3);
-    const int64_t g0 = ti.row0 + rr, g1 = g0 + 32;
-    if (g0 < ti.row_end) y[g0 * N + col] = f32_to_bf16_rne(acc0[v]);
-    if (g1 < ti.row_end) y[g1 * N + col] = f32_to_bf16_rne(acc1[v]);
+    const int64_t g = ti.row0 + hw * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+    if (g < ti.row_end) y[g * N + col] = f32_to_bf16_rne(acc[v]);
   }
 }
 

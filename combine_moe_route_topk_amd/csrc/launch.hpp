@@ -80,9 +80,7 @@ hipError_t launch_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidde
                                  const void* w_up, const void* w_down, int64_t ffn, void* y,
                                  void* workspace, hipStream_t stream);
 
-// fp8 block-scaled grouped GEMM: K / 128 scale blocks per row, at most this
-// many (the row scales of a 64-row tile are staged in LDS).
-constexpr int kMaxFp8Blocks = 128;
+// fp8 block-scaled grouped GEMM (K and N multiples of 128).
 hipError_t launch_grouped_gemm_fp8(const void* rows, const float* row_scales, int64_t n_rows,
                                    int64_t k_dim, const int32_t* expert_offsets, int n_experts,
                                    const void* w, const float* w_scales, int64_t n_dim, void* y,

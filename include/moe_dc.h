@@ -308,7 +308,7 @@ int moe_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
  *                   16-byte aligned
  * No workspace.  Errors: MOE_ERR_ARG for null pointers (unless n_rows == 0),
  * sizes < 1, misaligned scales; MOE_ERR_UNSUPPORTED for K % 128 != 0,
- * N % 128 != 0, K > 16384, E > MOE_MAX_EXPERTS or misaligned rows / w / y. */
+ * N % 128 != 0, E > MOE_MAX_EXPERTS or misaligned rows / w / y. */
 int moe_grouped_gemm_fp8(const void* rows, const float* row_scales, int64_t n_rows,
                          int64_t k_dim, const int32_t* expert_offsets, int32_t n_experts,
                          const void* w, const float* w_scales, int64_t n_dim, void* y,

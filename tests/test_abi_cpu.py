@@ -189,7 +189,6 @@ def test_grouped_gemm_fp8_errors():
     assert g(FAKE, FAKE, 8, 128, FAKE, 0, FAKE, FAKE, 128, FAKE, None) == ARG
     assert g(FAKE, FAKE, 8, 100, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == UNSUP      # K % 128
     assert g(FAKE, FAKE, 8, 128, FAKE, 4, FAKE, FAKE, 200, FAKE, None) == UNSUP      # N % 128
-    assert g(FAKE, FAKE, 8, 128 * 129, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == UNSUP  # K > 16384
     assert g(FAKE, FAKE, 8, 128, FAKE, 2000, FAKE, FAKE, 128, FAKE, None) == UNSUP   # E
     assert g(None, FAKE, 8, 128, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == ARG
     assert g(FAKE, FAKE, 8, 128, FAKE, 4, FAKE, None, 128, FAKE, None) == ARG
