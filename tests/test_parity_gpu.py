@@ -72,7 +72,8 @@ def test_route_full_size(name):
 
 
 @pytest.mark.parametrize("n,e,k", [(1, 1, 1), (7, 5, 3), (33, 64, 64), (100, 65, 8),
-                                   (64, 129, 2), (50, 1000, 32), (300, 1024, 8), (17, 256, 1)])
+                                   (64, 129, 2), (50, 1000, 32), (300, 1024, 8), (17, 256, 1),
+                                   (5, 256, 16), (3, 16, 16), (31, 255, 9), (1, 256, 8)])
 @pytest.mark.parametrize("renorm", [True, False])
 def test_route_shapes(n, e, k, renorm):
     rng = np.random.default_rng(n * 1000 + e)
