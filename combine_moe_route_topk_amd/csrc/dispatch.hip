@@ -677,6 +677,20 @@ size_t route_dispatch_workspace_bytes(int64_t n_tokens, int n_experts, int k, in
 
 hipError_t launch_route_dispatch(const RouteArgs& r, const DispatchArgs& a, hipStream_t stream) {
   if (a.n_tokens > 0) {
+    // identity layout (unsorted, one segment): the row copy needs nothing from
+    // the routing, so both run in one launch and only the maps follow
+    const bool identity = !a.sorted && a.n_segments == 1;
+    const uint64_t align = uint64_t(a.row_bytes) | reinterpret_cast<uintptr_t>(a.x) |
+                           reinterpret_cast<uintptr_t>(a.rows);
+    if (identity && a.x && !a.x_scales && (align & 15) == 0) {
+      hipError_t err = launch_route_copy_identity(r.logits, a.n_tokens, a.n_experts, a.k,
+                                                  r.renormalize, const_cast<int32_t*>(a.topk_idx),
+                                                  r.topk_w, a.x, a.row_bytes, a.rows, stream);
+      if (err != hipSuccess) return err;
+      DispatchArgs maps = a;
+      maps.x = nullptr;                     // rows are already in place
+      return launch_dispatch(maps, stream);
+    }
     hipError_t err = launch_route_topk(r.logits, a.n_tokens, a.n_experts, a.k, r.renormalize,
                                        const_cast<int32_t*>(a.topk_idx), r.topk_w, stream);
     if (err != hipSuccess) return err;

@@ -54,6 +54,13 @@ struct RouteArgs {
   int renormalize;
   float* topk_w;
 };
+// Routing and, side by side in the same launch, the identity-layout row copy
+// (unsorted, one segment): rows [N*k, row_bytes] with row t*k+j = x[t].
+// Requires 16-byte aligned x, rows and row_bytes; n_tokens > 0.
+hipError_t launch_route_copy_identity(const float* logits, int64_t n_tokens, int n_experts, int k,
+                                      int renormalize, int32_t* topk_idx, float* topk_w,
+                                      const void* x, int64_t row_bytes, void* rows,
+                                      hipStream_t stream);
 size_t route_dispatch_workspace_bytes(int64_t n_tokens, int n_experts, int k, int n_segments);
 hipError_t launch_route_dispatch(const RouteArgs& r, const DispatchArgs& a, hipStream_t stream);
 

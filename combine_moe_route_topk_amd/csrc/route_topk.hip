@@ -155,7 +155,90 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   }
 }
 
+// Routing and the identity-layout row copy in one launch.  With one segment
+// and no sort, pair t*k+j lands in row t*k+j ("backends/mlx: runtime MoE
+// expert-sort for decode (issue #20554)": the unsorted branch repeats each
+// token top_k times with identity inv_order), so the copy needs nothing from
+// the routing: workgroups [0, route_blocks) route (one wave per token) and
+// the rest copy (one wave per (token, 2 KB slice), 16-byte accesses), side by
+// side with no synchronisation between them.
+template <int R>
+__global__ __launch_bounds__(256) void route_copy_kernel(
+    const float* __restrict__ logits, int64_t n_tokens, int n_experts, int k, int renormalize,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int route_blocks,
+    const uint4* __restrict__ x, int64_t nvec, int n_slices, uint4* __restrict__ rows) {
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
+  const int blk = __builtin_amdgcn_readfirstlane(int(blockIdx.x));
+  if (blk < route_blocks) {
+    const int64_t t = int64_t(blk) * (256 / kWave) + w;
+    if (t >= n_tokens) return;
+    float val[R];
+    load_token<R>(logits + t * n_experts, n_experts, val);
+    int e;
+    float wt;
+    select_token<R>(val, n_experts, k, renormalize, e, wt);
+    if (lane < k) {
+      topk_idx[t * k + lane] = e;
+      topk_w[t * k + lane] = wt;
+    }
+    return;
+  }
+  constexpr int U = 2;
+  const int64_t item = int64_t(blk - route_blocks) * (256 / kWave) + w;
+  const int64_t t = item / n_slices;
+  if (t >= n_tokens) return;
+  const int64_t v0 = (item - t * n_slices) * int64_t(kWave * U) + lane;
+  const uint4* src = x + t * nvec;
+  uint4 buf[U];
+  int64_t vi[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    vi[u] = v0 + u * kWave < nvec ? v0 + u * kWave : nvec - 1;   // clamped lanes repeat a value
+    const unsigned int __attribute__((ext_vector_type(4))) q =
+        __builtin_nontemporal_load(reinterpret_cast<const unsigned int __attribute__((ext_vector_type(4)))*>(src + vi[u]));
+    buf[u] = make_uint4(q.x, q.y, q.z, q.w);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)   // wait for the loads once, before the stores
+    asm volatile("" : "+v"(buf[u].x), "+v"(buf[u].y), "+v"(buf[u].z), "+v"(buf[u].w));
+  uint4* dst = rows + t * int64_t(k) * nvec;
+  for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) dst[vi[u]] = buf[u];
+    dst += nvec;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_route_copy_identity(const float* logits, int64_t n_tokens, int n_experts, int k,
+                                      int renormalize, int32_t* topk_idx, float* topk_w,
+                                      const void* x, int64_t row_bytes, void* rows,
+                                      hipStream_t stream) {
+  constexpr int kBlock = 256, U = 2;
+  const int per_block = kBlock / kWave;
+  const int route_blocks = int((n_tokens + per_block - 1) / per_block);
+  const int64_t nvec = row_bytes / 16;
+  const int n_slices = int((nvec + kWave * U - 1) / (kWave * U));
+  const int64_t copy_blocks = (n_tokens * n_slices + per_block - 1) / per_block;
+  const dim3 grid(unsigned(route_blocks + copy_blocks));
+  const int r = (n_experts + kWave - 1) / kWave;
+#define MOE_ROUTE_COPY_CASE(RR)                                                              \
+  route_copy_kernel<RR><<<grid, kBlock, 0, stream>>>(                                       \
+      logits, n_tokens, n_experts, k, renormalize, topk_idx, topk_w, route_blocks,           \
+      static_cast<const uint4*>(x), nvec, n_slices, static_cast<uint4*>(rows));              \
+  break;
+  switch (r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : r <= 8 ? 8 : 16) {
+    case 1: MOE_ROUTE_COPY_CASE(1)
+    case 2: MOE_ROUTE_COPY_CASE(2)
+    case 4: MOE_ROUTE_COPY_CASE(4)
+    case 8: MOE_ROUTE_COPY_CASE(8)
+    default: MOE_ROUTE_COPY_CASE(16)
+  }
+#undef MOE_ROUTE_COPY_CASE
+  return hipGetLastError();
+}
 
 hipError_t launch_route_topk(const float* logits, int64_t n_tokens, int n_experts, int k,
                              int renormalize, int32_t* topk_idx, float* topk_w,

@@ -59,6 +59,10 @@ def test_prefill_shape(sort, g):
     (2100, 100, 9, 10, 0),
     (10, 16, 4, 4, 1),         # one-workgroup path
     (0, 16, 4, 4, 1),
+    (128, 256, 8, 1, 0),       # identity layout: routing and row copy in one launch
+    (37, 64, 3, 1, 0),
+    (1, 16, 16, 1, 0),
+    (5000, 1024, 8, 1, 0),     # identity layout, count + rank maps, 16 logits per lane
 ])
 def test_shapes(n, e, k, g, sort):
     rng = np.random.default_rng(n + e + k)
@@ -66,6 +70,14 @@ def test_shapes(n, e, k, g, sort):
     x = rng.integers(0, 2**16, (n, 24), dtype=np.uint16)
     _compare(logits, x, k, g, sort)
     _compare(logits, None, k, g, sort, renorm=False)
+
+
+@pytest.mark.parametrize("cols", [5, 12, 1000])   # 10-, 24- and 2000-byte rows: not 16-byte multiples
+def test_identity_layout_narrow_rows(cols):
+    rng = np.random.default_rng(cols)
+    logits = rng.standard_normal((70, 32)).astype(np.float32)
+    x = rng.integers(0, 2**16, (70, cols), dtype=np.uint16)
+    _compare(logits, x, 4, 1, 0)
 
 
 def test_fp8_segment_workload_and_auto_mode():
