@@ -397,7 +397,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build runs the single-GPU share of the path)", file=sys.stderr)
+              "(the path is timed on a single GPU's share of the work)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

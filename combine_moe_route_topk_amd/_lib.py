@@ -50,8 +50,8 @@ SIGNATURES = {
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m combine_moe_route_topk_amd.build` "
-            "(or __graft_entry__.build()); there is no CPU fallback")
+            f"{path} is missing: build it with `python combine_moe_route_topk_amd/build.py`; "
+            "there is no CPU fallback")
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

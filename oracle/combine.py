@@ -17,7 +17,7 @@ The oracle sums exactly and rounds once:
   sum |terms|, negligible beside the tolerances used -- returned unrounded so
   that the tests can apply the output format's rounding and tolerance.
 
-Tolerances (the tests apply them; the design doc derives them): fp32 output within
+Tolerances (the GPU tests apply them): fp32 output within
 1e-6 * sum_j |w_j * y_j| per element; bf16 output within one bf16 ulp of the
 correctly rounded exact value.
 

@@ -22,7 +22,7 @@ Sources.
   land in rank-major blocks that grouped GEMMs read in place -- read here as
   segment-major blocks, segment g = experts [g*E/G, (g+1)*E/G).
 
-Readings (also in the design doc): the argsort is stable (ties keep the flattened
+Readings: the argsort is stable (ties keep the flattened
 pair order t*k + j); sorted mode buckets by expert; unsorted mode buckets by
 segment (G = 1: one bucket, so the permutation is the identity); no capacity
 limit and no padding between blocks; ``dst_pos`` plays the role of

@@ -8,7 +8,7 @@ this ``[N, top_k]`` array) and fp32 routing weights.
 
 The pages never state the gating function; the workloads served here use
 softmax top-k with fp32 weights, renormalised over the selected experts.  The
-readings taken (each also listed in the design doc):
+readings taken:
 
 * selection is on the fp32 logits in the total order (value descending, then
   expert index ascending), with -0.0 == +0.0.  Softmax is strictly monotone,

@@ -13,7 +13,7 @@ Sources: "backends/mlx: runtime MoE expert-sort for decode (issue #20554)"
 that rows arrive grouped by expert, not a request to sort); "One-Sided
 Expert-Parallel All-to-All ... over NVLink" (abstract: grouped GEMMs read the
 dispatched buffers in place).  The SwiGLU form and the bf16 rounding of h
-between the two products are readings (DESIGN.md): the pages do not give the
+between the two products are readings: the pages do not give the
 expert's activation.
 
 Arithmetic: float64 on the bf16-valued inputs, h and y rounded once to bf16

@@ -1,6 +1,6 @@
 """Helpers for GPU tests: numpy <-> device tensors and the tolerance checks.
 
-The tolerances follow from the arithmetic (derivation in the design doc):
+The tolerances follow from the arithmetic:
 * fp32 combine output: |g - o| <= 1e-6 * sum_j |w_j y_j| (a k-term fp32 FMA
   chain is within gamma_k * sum|terms|, gamma_8 ~ 4.8e-7);
 * bf16 combine output: within one bf16 ulp of the correctly rounded exact
