@@ -53,8 +53,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l and l.strip()]
         if p.returncode != 0:
             failed.append((src, "\n".join(lines)))
-        elif verbose and lines:
-            print("\n".join(lines))
+        elif lines and (verbose or any("warning" in l for l in lines)):
+            print(f"[{src}]\n" + "\n".join(lines))
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n\n".join(f"[{s}]\n{t}" for s, t in failed))
     tmp = LIB + ".tmp"

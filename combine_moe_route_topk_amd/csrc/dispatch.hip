@@ -226,7 +226,6 @@ __global__ __launch_bounds__(kBlock) void rank_kernel(const int32_t* __restrict_
   __shared__ int s_wave[kWaves + 1];
   const int tid = threadIdx.x;
   const int w = tid / kWave;
-  const int lane = lane_id();
   const int me = blockIdx.x;
   const int per = n_experts / n_segments;
   const int n_buckets = sorted ? n_experts : n_segments;
@@ -620,7 +619,6 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int identity = (!a.sorted && a.n_segments == 1) ? 1 : 0;
-  const int per = a.n_experts / a.n_segments;
   const int n_buckets = a.sorted ? a.n_experts : a.n_segments;
   const int nbits = bits_for(n_buckets);
 

@@ -45,7 +45,6 @@ constexpr int kTM = 64;         // rows per tile
 constexpr int kTN = 128;        // columns per tile
 constexpr int kThreads = 512;   // 8 waves: 2 row halves x 4 column groups of 32
 constexpr int kXcds = 8;
-constexpr int kLoads = 4;       // 16-byte loads per operand row half per block
 
 struct Fp8Tile {
   int expert;
@@ -108,6 +107,9 @@ constexpr int kSlotBytes = kSlotS + kWaves * 256; // + each wave's copy of its 3
 constexpr int kDmaW = kTN * kQB / (kThreads * 16);   // 1 KB runs per wave: weights (2)
 constexpr int kDmaA = kTM * kQB / (kThreads * 16);   // rows (1)
 constexpr int kDmaPerStage = kDmaW + kDmaA + 1;      // + one run of row scales
+// Three 26 KB slots let two workgroups (16 waves) share a CU; deeper rings
+// (4 or 6 slots, one workgroup per CU) measured slower.
+constexpr int kRingSlots = 3;
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kQB + ((chunk ^ ((row >> 1) & 7)) << 4);
@@ -140,13 +142,21 @@ typedef const __attribute__((address_space(3))) unsigned char* lds_cptr;
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
   return uint32_t(size_t((lds_cptr)p));
 }
+// M0 is saved and restored around the load, so the compiler's own use of it
+// is undisturbed.
 __device__ __forceinline__ void dma16(const uint8_t* g, const unsigned char* l) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds_addr(l)), "v"(g) : "memory", "m0");
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep) : "s"(lds_addr(l)), "v"(g) : "memory");
 }
 __device__ __forceinline__ void dma4(const float* g, const unsigned char* l) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds_addr(l)), "v"(g) : "memory", "m0");
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep) : "s"(lds_addr(l)), "v"(g) : "memory");
 }
 
 // Direct global->LDS loads of K block `blk` into one ring slot (kDmaPerStage
@@ -211,26 +221,27 @@ __device__ __forceinline__ void block_mma(f32x16& acc, const unsigned char* slot
 // One K block: wait for block kt (only block kt+1's loads may be in flight),
 // then load block kt+2 into the slot block kt-1 used (every wave has passed
 // this barrier, so all its reads of that slot are done), then multiply.
-__device__ __forceinline__ void block_step(f32x16& acc, const unsigned char* cur, unsigned char* dst,
-                                           const Sources& src, int kt, int kb,
-                                           const float* __restrict__ swp, int w_row, int a_row,
-                                           int s_off, int half) {
-  block_barrier<wait_vm_lgkm0(kDmaPerStage)>();
+// One K block of a ring of NS slots: wait for block kt (the loads of blocks
+// kt+1 .. kt+NS-2 may still be in flight), then load block kt+NS-1 into the
+// slot block kt-1 used (every wave has passed this barrier, so all its reads
+// of that slot are done), then multiply.
+template <int NS>
+__device__ __forceinline__ void block_step(f32x16& acc, unsigned char* ring, const Sources& src,
+                                           int kt, int kb, const float* __restrict__ swp,
+                                           int w_row, int a_row, int s_off, int half) {
+  block_barrier<wait_vm_lgkm0((NS - 2) * kDmaPerStage)>();
   // past the last block the loads repeat it into a slot that is not multiplied
-  load_block(dst, src, min(kt + 2, kb - 1));
-  block_mma(acc, cur, w_row, a_row, s_off, half, swp[kt]);
+  load_block(ring + ((kt + NS - 1) % NS) * kSlotBytes, src, min(kt + NS - 1, kb - 1));
+  block_mma(acc, ring + (kt % NS) * kSlotBytes, w_row, a_row, s_off, half, swp[kt]);
 }
 
+template <int NS>   // LDS ring slots
 __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_kernel(
     const uint8_t* __restrict__ rows, const float* __restrict__ row_scales, int64_t n_rows,
     int K, const int32_t* __restrict__ offs, int n_experts, const uint8_t* __restrict__ w,
     const float* __restrict__ w_scales, int N, uint16_t* __restrict__ y, int max_m_tiles,
     int n_tiles) {
-  // three ring slots in distinct arrays, so the compiler can tell the slot
-  // being loaded from the slot being read and adds no wait between them
-  __shared__ __align__(1024) unsigned char slot0[kSlotBytes];
-  __shared__ __align__(1024) unsigned char slot1[kSlotBytes];
-  __shared__ __align__(1024) unsigned char slot2[kSlotBytes];
+  __shared__ __align__(1024) unsigned char ring[NS * kSlotBytes];
 
   const int nb = gridDim.x;                 // a multiple of kXcds
   const int b = blockIdx.x;
@@ -289,18 +300,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_kernel(
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-  load_block(slot0, src, 0);
-  load_block(slot1, src, min(1, kb - 1));
-  int kt = 0;
-  for (; kt + 3 <= kb; kt += 3) {
-    block_step(acc, slot0, slot2, src, kt, kb, swp, w_row, a_row, s_off, half);
-    block_step(acc, slot1, slot0, src, kt + 1, kb, swp, w_row, a_row, s_off, half);
-    block_step(acc, slot2, slot1, src, kt + 2, kb, swp, w_row, a_row, s_off, half);
-  }
-  if (kt < kb)           // kb % 3 >= 1
-    block_step(acc, slot0, slot2, src, kt, kb, swp, w_row, a_row, s_off, half);
-  if (kt + 1 < kb)       // kb % 3 == 2
-    block_step(acc, slot1, slot0, src, kt + 1, kb, swp, w_row, a_row, s_off, half);
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) load_block(ring + i * kSlotBytes, src, min(i, kb - 1));
+  for (int kt = 0; kt < kb; ++kt) block_step<NS>(acc, ring, src, kt, kb, swp, w_row, a_row, s_off, half);
   __builtin_amdgcn_s_waitcnt(wait_vm(0));   // no direct load may outlive the workgroup
 
   // acc[v] = C[8*(v/4) + 4*half + v%4][lane % 32] of the wave's 32 x 32 block
@@ -322,7 +324,7 @@ hipError_t launch_grouped_gemm_fp8(const void* rows, const float* row_scales, in
   const int n_tiles = int(n_dim / kTN);
   const int64_t tiles = int64_t(max_m_tiles) * n_tiles;
   const unsigned grid = unsigned((tiles + kXcds - 1) / kXcds * kXcds);
-  grouped_gemm_fp8_kernel<<<grid, kThreads, 0, stream>>>(
+  grouped_gemm_fp8_kernel<kRingSlots><<<grid, kThreads, 0, stream>>>(
       static_cast<const uint8_t*>(rows), row_scales, n_rows, int(k_dim), expert_offsets,
       n_experts, static_cast<const uint8_t*>(w), w_scales, int(n_dim),
       static_cast<uint16_t*>(y), max_m_tiles, n_tiles);
