@@ -35,9 +35,12 @@ constexpr int kRowMirror = 0x140;
 constexpr int kRowBcast15 = 0x142;
 constexpr int kRowBcast31 = 0x143;
 
+// One step of a DPP maximum.  Lanes outside ROW_MASK and lanes whose source
+// is out of range read 0, the identity of an unsigned maximum, so the move
+// folds into a single v_max_u32 with a DPP operand.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
-  const uint32_t o = uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), CTRL, ROW_MASK, 0xF, false));
+  const uint32_t o = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROW_MASK, 0xF, true));
   return o > v ? o : v;
 }
 
