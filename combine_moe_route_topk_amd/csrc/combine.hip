@@ -196,7 +196,25 @@ hipError_t launch_combine_typed(const void* y, int64_t n_tokens, int64_t hidden,
   const int64_t nk = n_tokens * k;
   const int per_block = kBlock / kWave;
   const bool aligned = ((reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
-  if (hidden % kGroup == 0 && aligned) {
+  // Fewer than 4096 two-kilobyte items (decode-sized batches): 1 KB slices
+  // double the waves of a launch that is latency-bound, not bandwidth-bound.
+  if (hidden % kGroup == 0 && aligned && n_tokens * ((hidden / kGroup + 127) / 128) < 4096) {
+    constexpr int U = 1;
+    const int64_t ngroups = hidden / kGroup;
+    const int n_slices = int((ngroups + kWave * U - 1) / (kWave * U));
+    const int64_t items = n_tokens * n_slices;
+    const unsigned blocks = unsigned((items + per_block - 1) / per_block);
+    const TY* yy = static_cast<const TY*>(y);
+    TO* oo = static_cast<TO*>(out);
+    if (k >= 8)
+      combine_kernel<TY, TO, U, 8><<<blocks, kBlock, 0, stream>>>(yy, n_tokens, hidden, k, n_slices, dst_pos, topk_w, nk, oo);
+    else if (k >= 4)
+      combine_kernel<TY, TO, U, 4><<<blocks, kBlock, 0, stream>>>(yy, n_tokens, hidden, k, n_slices, dst_pos, topk_w, nk, oo);
+    else if (k >= 2)
+      combine_kernel<TY, TO, U, 2><<<blocks, kBlock, 0, stream>>>(yy, n_tokens, hidden, k, n_slices, dst_pos, topk_w, nk, oo);
+    else
+      combine_kernel<TY, TO, U, 1><<<blocks, kBlock, 0, stream>>>(yy, n_tokens, hidden, k, n_slices, dst_pos, topk_w, nk, oo);
+  } else if (hidden % kGroup == 0 && aligned) {
     constexpr int U = 2;
     const int64_t ngroups = hidden / kGroup;
     const int n_slices = int((ngroups + kWave * U - 1) / (kWave * U));

@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 // the routing: workgroups [0, route_blocks) route (one wave per token) and
 // the rest copy (one wave per (token, 2 KB slice), 16-byte accesses), side by
 // side with no synchronisation between them.
-template <int R>
+template <int R, int U>
 __global__ __launch_bounds__(256) void route_copy_kernel(
     const float* __restrict__ logits, int64_t n_tokens, int n_experts, int k, int renormalize,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int route_blocks,
@@ -187,7 +187,6 @@ __global__ __launch_bounds__(256) void route_copy_kernel(
     }
     return;
   }
-  constexpr int U = 2;
   const int64_t item = int64_t(blk - route_blocks) * (256 / kWave) + w;
   const int64_t t = item / n_slices;
   if (t >= n_tokens) return;
@@ -219,18 +218,26 @@ hipError_t launch_route_copy_identity(const float* logits, int64_t n_tokens, int
                                       int renormalize, int32_t* topk_idx, float* topk_w,
                                       const void* x, int64_t row_bytes, void* rows,
                                       hipStream_t stream) {
-  constexpr int kBlock = 256, U = 2;
+  constexpr int kBlock = 256;
   const int per_block = kBlock / kWave;
   const int route_blocks = int((n_tokens + per_block - 1) / per_block);
   const int64_t nvec = row_bytes / 16;
+  // decode-sized batches: 1 KB copy slices (twice the waves) instead of 2 KB
+  const bool small = n_tokens * ((nvec + 127) / 128) < 4096;
+  const int U = small ? 1 : 2;
   const int n_slices = int((nvec + kWave * U - 1) / (kWave * U));
   const int64_t copy_blocks = (n_tokens * n_slices + per_block - 1) / per_block;
   const dim3 grid(unsigned(route_blocks + copy_blocks));
   const int r = (n_experts + kWave - 1) / kWave;
 #define MOE_ROUTE_COPY_CASE(RR)                                                              \
-  route_copy_kernel<RR><<<grid, kBlock, 0, stream>>>(                                       \
-      logits, n_tokens, n_experts, k, renormalize, topk_idx, topk_w, route_blocks,           \
-      static_cast<const uint4*>(x), nvec, n_slices, static_cast<uint4*>(rows));              \
+  if (small)                                                                                 \
+    route_copy_kernel<RR, 1><<<grid, kBlock, 0, stream>>>(                                  \
+        logits, n_tokens, n_experts, k, renormalize, topk_idx, topk_w, route_blocks,         \
+        static_cast<const uint4*>(x), nvec, n_slices, static_cast<uint4*>(rows));            \
+  else                                                                                       \
+    route_copy_kernel<RR, 2><<<grid, kBlock, 0, stream>>>(                                  \
+        logits, n_tokens, n_experts, k, renormalize, topk_idx, topk_w, route_blocks,         \
+        static_cast<const uint4*>(x), nvec, n_slices, static_cast<uint4*>(rows));            \
   break;
   switch (r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : r <= 8 ? 8 : 16) {
     case 1: MOE_ROUTE_COPY_CASE(1)

@@ -63,6 +63,8 @@ def test_prefill_shape(sort, g):
     (37, 64, 3, 1, 0),
     (1, 16, 16, 1, 0),
     (5000, 1024, 8, 1, 0),     # identity layout, count + rank maps, 16 logits per lane
+    (50, 8, 1, 1, 0),          # identity layout, k = 1
+    (9, 1, 1, 1, 0),           # one expert
 ])
 def test_shapes(n, e, k, g, sort):
     rng = np.random.default_rng(n + e + k)
