@@ -265,7 +265,7 @@ def time_all_configs(torch, moe, steps, warmup):
     return out
 
 
-def time_swiglu(torch, moe, steps=10, warmup=2):
+def time_swiglu(torch, moe, steps=10, warmup=2, cpu=False):
     """The Mixtral-like layer's grouped SwiGLU (N=8192, k=2 -> 16384 rows,
     D=4096, F=14336, E=8) reading the sorted dispatch in place."""
     from workloads import CONFIGS, make_inputs, make_swiglu_weights_device
@@ -296,12 +296,15 @@ def time_swiglu(torch, moe, steps=10, warmup=2):
     ms = e0.elapsed_time(e1) / steps
     flop = 2.0 * rows * cfg.hidden * cfg.ffn * 3
     tflops = flop / (ms * 1e-3) / 1e12
-    return {"workload": f"mixtral: {cfg.note}", "rows": rows, "ms": round(ms, 3),
-            "tflops": round(tflops, 1), "peak_tflops": 2500.0, "frac": round(tflops / 2500.0, 4),
-            "flop": flop, "dtype": "bf16 in, fp32 accumulate"}
+    out = {"workload": f"mixtral: {cfg.note}", "rows": rows, "ms": round(ms, 3),
+           "tflops": round(tflops, 1), "peak_tflops": 2500.0, "frac": round(tflops / 2500.0, 4),
+           "flop": flop, "dtype": "bf16 in, fp32 accumulate"}
+    if cpu:
+        out["cpu_oracle"] = cpu_oracle_swiglu(torch, res, w)
+    return out
 
 
-def time_fp8_gemm(torch, moe, steps=10, warmup=2):
+def time_fp8_gemm(torch, moe, steps=10, warmup=2, cpu=False):
     """The segment-major workload's fp8 expert projection (N_out = 4096, K =
     7168, 256 experts): the sorted fp8 dispatch's rows and 1x128 scales read in
     place by the block-scaled grouped GEMM.  Weight streaming dominates."""
@@ -342,12 +345,70 @@ def time_fp8_gemm(torch, moe, steps=10, warmup=2):
            "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
            "tflops": round(flop / (ms * 1e-3) / 1e12, 1), "flop": flop,
            "bound": "hbm (weights)", "dtype": "fp8 e4m3fn in, fp32 accumulate, bf16 out"}
+    if cpu:
+        out["cpu_oracle"] = cpu_oracle_fp8_gemm(torch, res, wt)
     del wt, y, res, x, xs
     torch.cuda.empty_cache()
     return out
 
 
 # ------------------------------------------------------------------ CPU baseline
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def _time_oracle(fn, min_seconds=10.0, max_repeats=5):
+    times = []
+    while len(times) < max_repeats and (len(times) < 1 or sum(times) < min_seconds):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), len(times), sum(times)
+
+
+def cpu_oracle_swiglu(torch, res, w, n_sample=128):
+    """The oracle's SwiGLU on the first rows of expert 0 (its weights copied
+    back from the device), timed on the host."""
+    from oracle.swiglu import swiglu_rows
+    offs = res.expert_offsets.cpu().numpy()
+    m = int(min(n_sample, offs[1] - offs[0]))
+    rows = res.rows[int(offs[0]):int(offs[0]) + m].view(torch.int16).cpu().numpy().view(np.uint16)
+    host = {k: v[0:1].view(torch.int16).cpu().numpy().view(np.uint16) for k, v in w.items()}
+    experts = np.zeros(m, np.int64)
+    dt, n, tot = _time_oracle(lambda: swiglu_rows(rows, experts, host["w_gate"], host["w_up"], host["w_down"]))
+    f, d = host["w_gate"].shape[1], host["w_gate"].shape[2]
+    return dict(value=round(2.0 * m * d * 3 * f / dt / 1e12, 5), unit="TFLOP/s", cores=_blas_threads(),
+                kind="oracle", sample=f"{m} rows of expert 0, float64 numpy (BLAS matmul); median of {n} "
+                                      f"passes ({tot:.1f} s)", seconds_per_pass=round(dt, 3))
+
+
+def cpu_oracle_fp8_gemm(torch, res, wt, n_experts_sample=2):
+    """The oracle's fp8 block-scaled GEMM on every row of the first experts
+    that own rows (their weights copied back), timed on the host; GB/s of the
+    sample's algorithmic bytes."""
+    from oracle.gemm_fp8 import gemm_fp8_rows
+    offs = res.expert_offsets.cpu().numpy()
+    busy = [e for e in range(offs.size - 1) if offs[e + 1] > offs[e]][:n_experts_sample]
+    sel = np.concatenate([np.arange(offs[e], offs[e + 1]) for e in busy])
+    experts = np.concatenate([np.full(offs[e + 1] - offs[e], j) for j, e in enumerate(busy)])
+    rows = res.rows.cpu().numpy()[sel]
+    sx = res.row_scales.cpu().numpy()[sel]
+    idx = torch.tensor(busy, device=wt["w"].device)
+    w = wt["w"].index_select(0, idx).cpu().numpy()
+    sw = wt["w_scales"].index_select(0, idx).cpu().numpy()
+    dt, n, tot = _time_oracle(lambda: gemm_fp8_rows(rows, sx, experts, w, sw))
+    nn, k = w.shape[1], w.shape[2]
+    b = len(busy) * (nn * k + sw[0].size * 4) + sel.size * (k + sx.shape[1] * 4) + sel.size * nn * 2
+    return dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=_blas_threads(), kind="oracle",
+                sample=f"all {sel.size} rows of experts {busy}, float64 numpy; median of {n} passes "
+                       f"({tot:.1f} s)", seconds_per_pass=round(dt, 3))
+
 
 def cpu_baseline(cfg, n_sample, min_seconds=10.0, max_repeats=5):
     """The oracle as it stands, on the first ``n_sample`` tokens of the same
@@ -478,9 +539,9 @@ def main():
     if not args.no_all and args.workload == "prefill":
         rec["all_configs"] = time_all_configs(torch, moe, args.steps, args.warmup)
     if not args.no_gemm and args.workload == "prefill":
-        rec["grouped_swiglu"] = time_swiglu(torch, moe)
+        rec["grouped_swiglu"] = time_swiglu(torch, moe, cpu=not args.no_cpu_baseline)
         torch.cuda.empty_cache()
-        rec["grouped_gemm_fp8"] = time_fp8_gemm(torch, moe)
+        rec["grouped_gemm_fp8"] = time_fp8_gemm(torch, moe, cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
     print(json.dumps(rec), flush=True)
