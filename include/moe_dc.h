@@ -191,6 +191,8 @@ size_t moe_route_dispatch_workspace_bytes(int64_t n_tokens, int32_t n_experts, i
  *   logits [N, E] f32, renormalize, topk_idx [N, k] i32 (output, then read
  *   by the dispatch), topk_w [N, k] f32 (output); every other argument as in
  *   moe_dispatch; workspace of moe_route_dispatch_workspace_bytes(N, E, k, G).
+ * In the identity layout (unsorted, G == 1) row t*k+j is x[t] whatever the
+ * routing chooses, so the routing and the row copy run in one launch.
  * Errors: those of moe_route_topk and moe_dispatch. */
 int moe_route_dispatch(const float* logits, int32_t renormalize, int32_t* topk_idx, float* topk_w,
                        const void* x, const float* x_scales, int32_t dtype, int64_t n_tokens,
