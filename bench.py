@@ -352,6 +352,73 @@ def time_fp8_gemm(torch, moe, steps=10, warmup=2, cpu=False):
     return out
 
 
+def time_gather_swiglu(torch, moe, steps=10, warmup=2, cpu=False):
+    """Decode with real experts (N=128, D=7168, E=256, top-8, F=2048): the
+    unsorted identity-layout rows read where the dispatch left them by the
+    per-row-expert SwiGLU.  Every active expert's three [F, D] matrices are
+    streamed once, which dominates the bytes.  Timed alone and as the whole
+    layer (route + unsorted dispatch + expert FFN + combine)."""
+    from workloads import DECODE_FFN, make_inputs, make_swiglu_weights_device
+    cfg = DECODE_FFN
+    inp = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    w = make_swiglu_weights_device(cfg)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    idx, tw, res = moe.moe_route_dispatch(logits, x, cfg.top_k, cfg.n_segments, cfg.renormalize,
+                                          cfg.sort, cfg.sort_cutoff)
+    rows = res.rows.shape[0]
+    e, d, f = cfg.n_experts, cfg.hidden, cfg.ffn
+    ws = torch.empty(moe.moe_gather_swiglu_workspace_bytes(rows, e, d, f), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty_like(res.rows)
+    ffn = lambda: moe.moe_gather_swiglu(res.rows, res.row_expert, w["w_gate"], w["w_up"],
+                                        w["w_down"], y=y, workspace=ws)
+    rd_ws = torch.empty(moe.moe_route_dispatch_workspace_bytes(cfg.n_tokens, e, cfg.top_k, 1),
+                        dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+
+    def layer():
+        moe.moe_route_dispatch(logits, x, cfg.top_k, cfg.n_segments, cfg.renormalize, cfg.sort,
+                               cfg.sort_cutoff, topk_idx=idx, topk_w=tw, workspace=rd_ws, out=res)
+        ffn()
+        moe.moe_combine(y, res.dst_pos, tw, out=out)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(ffn)
+    ms_layer = timed(layer)
+    counts = res.expert_counts.cpu().numpy()
+    active = int((counts > 0).sum())
+    wbytes = active * 3 * f * d * 2
+    b = wbytes + rows * d * 2 + rows * 4 + 2 * rows * f * 2 + rows * d * 2
+    gbs = b / (ms * 1e-3) / 1e9
+    rec = {"workload": f"decode_ffn: {cfg.note}", "rows": rows, "active_experts": active,
+           "max_rows_per_expert": int(counts.max()), "ms": round(ms, 3), "bytes": b,
+           "weight_bytes": wbytes, "GB_per_s": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "layer_ms": round(ms_layer, 3),
+           "layer_calls": "moe_route_dispatch (unsorted, with rows) + moe_gather_swiglu + moe_combine",
+           "bound": "hbm (weights)", "dtype": "bf16 in, fp32 accumulate, bf16 out"}
+    if cpu:
+        rec["cpu_oracle"] = cpu_oracle_gather_swiglu(torch, res, w)
+    del w, y, ws, res, x, logits
+    torch.cuda.empty_cache()
+    return rec
+
+
 # ------------------------------------------------------------------ CPU baseline
 
 def _blas_threads():
@@ -408,6 +475,28 @@ def cpu_oracle_fp8_gemm(torch, res, wt, n_experts_sample=2):
     return dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=_blas_threads(), kind="oracle",
                 sample=f"all {sel.size} rows of experts {busy}, float64 numpy; median of {n} passes "
                        f"({tot:.1f} s)", seconds_per_pass=round(dt, 3))
+
+
+def cpu_oracle_gather_swiglu(torch, res, w, n_experts_sample=2):
+    """The oracle's row-by-row SwiGLU on every row of the first experts that
+    own rows (their weights copied back), timed on the host; GB/s of the
+    sample's algorithmic bytes."""
+    from oracle.swiglu import swiglu_rows
+    rexp = res.row_expert.cpu().numpy()
+    busy = np.unique(rexp)[:n_experts_sample]
+    sel = np.nonzero(np.isin(rexp, busy))[0]
+    rows = res.rows.view(torch.int16).cpu().numpy().view(np.uint16)[sel]
+    local = np.searchsorted(busy, rexp[sel])
+    idx = torch.tensor(busy, device=w["w_gate"].device)
+    host = {k: v.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+            for k, v in w.items()}
+    dt, n, tot = _time_oracle(lambda: swiglu_rows(rows, local, host["w_gate"], host["w_up"],
+                                                  host["w_down"]))
+    f, d = host["w_gate"].shape[1], host["w_gate"].shape[2]
+    b = len(busy) * 3 * f * d * 2 + sel.size * (d * 2 + 4 + 2 * f * 2 + d * 2)
+    return dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=_blas_threads(), kind="oracle",
+                sample=f"all {sel.size} rows of experts {busy.tolist()}, float64 numpy; median "
+                       f"of {n} passes ({tot:.1f} s)", seconds_per_pass=round(dt, 3))
 
 
 def cpu_baseline(cfg, n_sample, min_seconds=10.0, max_repeats=5):
@@ -542,6 +631,8 @@ def main():
         rec["grouped_swiglu"] = time_swiglu(torch, moe, cpu=not args.no_cpu_baseline)
         torch.cuda.empty_cache()
         rec["grouped_gemm_fp8"] = time_fp8_gemm(torch, moe, cpu=not args.no_cpu_baseline)
+        torch.cuda.empty_cache()
+        rec["gather_swiglu"] = time_gather_swiglu(torch, moe, cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
     print(json.dumps(rec), flush=True)

@@ -43,6 +43,9 @@ SIGNATURES = {
     "moe_grouped_swiglu_workspace_bytes": (_sz, [_i64, _i32, _i64, _i64]),
     "moe_grouped_swiglu": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _p, _i64, _p, _p,
                                           _sz, _p]),
+    "moe_gather_swiglu_workspace_bytes": (_sz, [_i64, _i32, _i64, _i64]),
+    "moe_gather_swiglu": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _p, _i64, _p, _p,
+                                         _sz, _p]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _i32, _p, _p, _i64, _p, _p]),
 }
 

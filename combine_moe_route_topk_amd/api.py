@@ -293,6 +293,39 @@ def moe_grouped_swiglu(rows: torch.Tensor, expert_offsets: torch.Tensor, w_gate:
     return y
 
 
+def moe_gather_swiglu_workspace_bytes(n_rows: int, n_experts: int, hidden: int, ffn: int) -> int:
+    return int(lib.moe_gather_swiglu_workspace_bytes(n_rows, n_experts, hidden, ffn))
+
+
+def moe_gather_swiglu(rows: torch.Tensor, row_expert: torch.Tensor, w_gate: torch.Tensor,
+                      w_up: torch.Tensor, w_down: torch.Tensor, y: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rows [R, D] bf16 in any order, row_expert [R] int32 (the expert of each
+    row); w_gate/w_up [E, F, D], w_down [E, D, F] bf16 -> y [R, D] bf16, row r
+    computed with expert row_expert[r] (rows with an id outside [0, E) keep
+    what y held)."""
+    _need(rows, "rows", (torch.bfloat16,))
+    dev = rows.device
+    for name, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, name, (torch.bfloat16,), dev)
+    _need(row_expert, "row_expert", (torch.int32,), dev)
+    r, d = rows.shape
+    e, f, d2 = w_gate.shape
+    if d2 != d or tuple(w_up.shape) != (e, f, d) or tuple(w_down.shape) != (e, d, f) or \
+            row_expert.numel() != r:
+        raise ValueError("moe_gather_swiglu: inconsistent shapes")
+    if y is None:
+        y = torch.empty_like(rows)
+    _need(y, "y", (torch.bfloat16,), dev)
+    if workspace is None:
+        workspace = torch.empty(max(moe_gather_swiglu_workspace_bytes(r, e, d, f), 256),
+                                dtype=torch.uint8, device=dev)
+    check("moe_gather_swiglu", lib.moe_gather_swiglu(
+        _ptr(rows), r, d, _ptr(row_expert), e, _ptr(w_gate), _ptr(w_up), _ptr(w_down), f,
+        _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return y
+
+
 def moe_grouped_gemm_fp8(rows: torch.Tensor, row_scales: torch.Tensor, expert_offsets: torch.Tensor,
                          w: torch.Tensor, w_scales: torch.Tensor, y: Optional[torch.Tensor] = None,
                          stream=None) -> torch.Tensor:

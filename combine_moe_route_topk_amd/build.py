@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_dc.so")
 SOURCES = ["api.cpp", "route_topk.hip", "dispatch.hip", "combine.hip", "grouped_swiglu.hip",
-           "grouped_gemm_fp8.hip"]
+           "grouped_gemm_fp8.hip", "gather_swiglu.hip"]
 ARCH = "gfx950"
 
 

@@ -56,4 +56,34 @@ __device__ __forceinline__ float wave_reduce_sum(float v) {
   return v;
 }
 
+// Exclusive scan of one int per thread over a workgroup of up to 1024
+// threads; returns the exclusive prefix and writes the total to *total.
+// s_wave holds (waves + 1) ints of LDS; every thread of the workgroup calls it.
+__device__ inline int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) s_wave[w] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < nw; ++i) {
+      const int c = s_wave[i];
+      s_wave[i] = run;
+      run += c;
+    }
+    s_wave[nw] = run;
+  }
+  __syncthreads();
+  const int excl = s_wave[w] + incl - v;
+  *total = s_wave[nw];
+  return excl;
+}
+
 }  // namespace moe

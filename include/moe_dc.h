@@ -288,6 +288,38 @@ int moe_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                        const void* w_gate, const void* w_up, const void* w_down, int64_t ffn,
                        void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_gather_swiglu_workspace_bytes -- workspace of moe_gather_swiglu. */
+size_t moe_gather_swiglu_workspace_bytes(int64_t n_rows, int32_t n_experts, int64_t hidden,
+                                         int64_t ffn);
+
+/* moe_gather_swiglu -- the expert FFN of moe_grouped_swiglu over rows left in
+ * any order, each row naming its own expert ([ET-PR]: decode keeps the rows in
+ * token order, with no argsort, and the expert product takes a per-row expert
+ * id, gather_mm with unsorted right-hand indices).  For every row r with
+ * e = row_expert[r] in [0, E):
+ *   h = bf16( silu(W_gate[e] rows[r]) * (W_up[e] rows[r]) )
+ *   y[r] = bf16( W_down[e] h )
+ * Rows whose id lies outside [0, E) are skipped: their y rows are left as they
+ * were.  The rows are not moved: a stable counting sort of the ids lists each
+ * expert's rows, every active expert's weights are read once for all of them,
+ * and y[r] lands at row r.  Meant for few rows per expert (decode); grouped
+ * rows at prefill sizes are the case of moe_grouped_swiglu.
+ *
+ *   rows            [n_rows, D] bfloat16, any order (e.g. the unsorted dispatch)
+ *   row_expert      [n_rows] int32, device-resident
+ *   w_gate, w_up    [E, F, D] bfloat16;  w_down [E, D, F] bfloat16
+ *   y               [n_rows, D] bfloat16, output, same row order as rows
+ *   workspace       moe_gather_swiglu_workspace_bytes(n_rows, E, D, F) bytes
+ * Errors: MOE_ERR_ARG for null pointers (unless n_rows == 0), n_rows < 0,
+ * sizes < 1; MOE_ERR_UNSUPPORTED for D % 128 != 0, F % 128 != 0,
+ * E > MOE_MAX_EXPERTS, n_rows beyond the int32 range, rows or a weight tensor
+ * not 16-byte aligned, y not 2-byte aligned;
+ * MOE_ERR_WORKSPACE for a short workspace or one not 256-byte aligned. */
+int moe_gather_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
+                      const int32_t* row_expert, int32_t n_experts,
+                      const void* w_gate, const void* w_up, const void* w_down, int64_t ffn,
+                      void* y, void* workspace, size_t workspace_bytes, void* stream);
+
 /* moe_grouped_gemm_fp8 -- fp8 block-scaled grouped expert GEMM reading the
  * dispatched fp8 rows in place ([1SIDED]: the dispatch is agnostic to the
  * activation quantisation format, and grouped GEMMs read the received buffers

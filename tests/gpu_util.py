@@ -6,7 +6,12 @@ The tolerances follow from the arithmetic:
 * bf16 combine output: within one bf16 ulp of the correctly rounded exact
   value, or, where the terms cancel, within the fp32 bound plus half a bf16
   ulp of the result;
-* routing weights: 1e-6 relative (a handful of fp32 roundings plus expf).
+* routing weights: 1e-6 relative (a handful of fp32 roundings plus expf);
+* SwiGLU expert FFN (bf16 inputs, fp32 accumulation, h rounded to bf16 on
+  both sides): every element within 2e-2 * max(|o|, rms of its row), and each
+  expert's relative Frobenius error within 2e-2.  A flipped bf16 rounding of
+  one h element moves y by far less; a wrong expert, a dropped K chunk or a
+  swapped gate/up moves whole rows by O(1) relative.
 """
 from __future__ import annotations
 
@@ -71,3 +76,16 @@ def combine_reference(y_rows_f32: np.ndarray, dst_pos: np.ndarray, w: np.ndarray
     exact = combine_f64(y_rows_f32, dst_pos, w, k, tokens=tokens)
     mag = combine_f64(np.abs(y_rows_f32), dst_pos, np.abs(w), k, tokens=tokens)
     return exact, mag
+
+
+def check_swiglu(got_bits, ref_bits, experts, what=""):
+    g = codecs.bf16_bits_to_f32(got_bits).astype(np.float64)
+    o = codecs.bf16_bits_to_f32(ref_bits).astype(np.float64)
+    rms = np.sqrt(np.mean(o * o, axis=1, keepdims=True))
+    bound = 2e-2 * np.maximum(np.abs(o), rms)
+    bad = np.abs(g - o) > bound
+    assert not bad.any(), f"{what}: {bad.sum()} elements outside 2e-2"
+    for e in np.unique(experts):
+        sel = experts == e
+        rel = np.linalg.norm(g[sel] - o[sel]) / max(np.linalg.norm(o[sel]), 1e-30)
+        assert rel <= 2e-2, f"{what}: expert {e} relative error {rel:.3e}"

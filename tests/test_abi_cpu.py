@@ -199,3 +199,31 @@ def test_grouped_gemm_fp8_errors():
     assert g(FAKE, FAKE, 8, 128, FAKE, 4, FAKE, FAKE, 128, odd, None) == UNSUP
     assert g(FAKE, ctypes.c_void_p(0x1002), 8, 128, FAKE, 4, FAKE, FAKE, 128, FAKE, None) == ARG
     assert b"aligned" in lib.moe_last_error()
+
+
+def test_gather_swiglu_errors():
+    g = lib.moe_gather_swiglu
+    ws = lib.moe_gather_swiglu_workspace_bytes(1024, 256, 7168, 2048)
+    assert ws >= 1024 * 2048 * 2                                      # h
+    assert lib.moe_gather_swiglu_workspace_bytes(-1, 8, 128, 128) == 0
+    assert lib.moe_gather_swiglu_workspace_bytes(8, 2000, 128, 128) == 0
+    assert g(FAKE, -1, 128, FAKE, 4, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 20, None) == ARG
+    assert g(FAKE, 8, 0, FAKE, 4, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 20, None) == ARG
+    assert g(FAKE, 8, 128, FAKE, 0, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 20, None) == ARG
+    assert g(FAKE, 8, 128, FAKE, 2000, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 20, None) == UNSUP
+    assert g(FAKE, 8, 192, FAKE, 4, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 20, None) == UNSUP
+    assert g(FAKE, 8, 128, FAKE, 4, FAKE, FAKE, FAKE, 64, FAKE, FAKE, 1 << 20, None) == UNSUP
+    assert g(FAKE, 1 << 31, 128, FAKE, 4, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 20, None) == UNSUP
+    assert g(None, 8, 128, FAKE, 4, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 20, None) == ARG
+    assert g(FAKE, 8, 128, None, 4, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 20, None) == ARG
+    odd = ctypes.c_void_p(0x1008)
+    assert g(odd, 8, 128, FAKE, 4, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 20, None) == UNSUP
+    assert g(FAKE, 8, 128, FAKE, 4, FAKE, odd, FAKE, 128, FAKE, FAKE, 1 << 20, None) == UNSUP
+    assert g(FAKE, 8, 128, FAKE, 4, FAKE, FAKE, FAKE, 128, ctypes.c_void_p(0x1001), FAKE,
+             1 << 20, None) == UNSUP
+    need = lib.moe_gather_swiglu_workspace_bytes(8, 4, 128, 128)
+    assert g(FAKE, 8, 128, FAKE, 4, FAKE, FAKE, FAKE, 128, FAKE, FAKE, need - 1, None) == WS
+    assert g(FAKE, 8, 128, FAKE, 4, FAKE, FAKE, FAKE, 128, FAKE, None, need, None) == WS
+    assert g(FAKE, 8, 128, FAKE, 4, FAKE, FAKE, FAKE, 128, FAKE, ctypes.c_void_p(0x1080), need,
+             None) == WS
+    assert g(None, 0, 128, None, 4, None, None, None, 128, None, None, 0, None) == 0   # empty

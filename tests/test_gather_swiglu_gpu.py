@@ -1,0 +1,136 @@
+"""SwiGLU experts over rows in any order (per-row expert ids) against the
+oracle's row-by-row definition (oracle.swiglu.swiglu_rows); tolerance in
+tests.gpu_util.check_swiglu."""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_route_topk_amd as moe
+from oracle import codecs
+from oracle.combine import combine_f64
+from oracle.swiglu import swiglu_rows
+from tests.gpu_util import DEV, check_combine, check_swiglu, to_dev, to_np
+from workloads import DECODE_FFN, make_inputs, make_swiglu_weights_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(a):
+    return codecs.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def _weights(rng, e, d, f, std=0.05):
+    return (_bf16(rng.standard_normal((e, f, d)) * std), _bf16(rng.standard_normal((e, f, d)) * std),
+            _bf16(rng.standard_normal((e, d, f)) * std))
+
+
+def _run(rows, experts, w, y=None):
+    out = moe.moe_gather_swiglu(to_dev(rows), to_dev(np.asarray(experts, np.int32)),
+                                *map(to_dev, w), y=y)
+    torch.cuda.synchronize()
+    return to_np(out)
+
+
+@pytest.mark.parametrize("e,d,f,counts", [
+    (4, 128, 128, [5, 0, 1, 31]),              # empty expert, 1 row, two passes (16 + 15)
+    (8, 256, 384, [16, 17, 0, 3, 48, 1, 0, 9]),  # exact pass, pass + 1, three passes
+    (3, 384, 256, [7, 33, 2]),                 # K = 384: three 128-chunks on gate/up
+    (2, 640, 128, [20, 4]),                    # five chunks; down has one chunk (K = 128)
+    (16, 128, 512, [1] * 16),                  # one row per expert, partial down group
+    (1, 512, 256, [70]),                       # a single expert, five passes
+])
+def test_gather_swiglu_small(e, d, f, counts):
+    rng = np.random.default_rng(d + 7 * f + e)
+    experts = rng.permutation(np.repeat(np.arange(e), counts)).astype(np.int32)   # unsorted
+    rows = _bf16(rng.standard_normal((experts.size, d)))
+    w = _weights(rng, e, d, f)
+    got = _run(rows, experts, w)
+    ref = swiglu_rows(rows, experts, *w)
+    check_swiglu(got, ref, experts, what=f"E={e} D={d} F={f}")
+
+
+def test_gather_swiglu_matches_grouped_rows_either_order():
+    """The same rows in expert-major order and shuffled: each row's output
+    depends only on the row and its expert."""
+    rng = np.random.default_rng(3)
+    e, d, f = 6, 256, 256
+    experts = np.repeat(np.arange(e), [3, 20, 0, 1, 40, 9]).astype(np.int32)
+    rows = _bf16(rng.standard_normal((experts.size, d)))
+    w = _weights(rng, e, d, f)
+    perm = rng.permutation(experts.size)
+    a = _run(rows, experts, w)
+    b = _run(rows[perm], experts[perm], w)
+    assert np.array_equal(a[perm], b)
+    check_swiglu(a, swiglu_rows(rows, experts, *w), experts, what="grouped order")
+
+
+def test_gather_swiglu_skips_out_of_range_ids():
+    rng = np.random.default_rng(4)
+    e, d, f = 3, 128, 128
+    experts = np.array([0, -1, 2, 3, 1, 1, 99, 0, -7, 2], np.int32)
+    rows = _bf16(rng.standard_normal((experts.size, d)))
+    w = _weights(rng, e, d, f)
+    y = torch.full((experts.size, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    got = _run(rows, experts, w, y=y)
+    bad = (experts < 0) | (experts >= e)
+    assert (codecs.bf16_bits_to_f32(got[bad]) == 7.0).all()
+    ok = ~bad
+    check_swiglu(got[ok], swiglu_rows(rows[ok], experts[ok], *w), experts[ok], what="in range")
+
+
+def test_gather_swiglu_deterministic_and_empty():
+    rng = np.random.default_rng(5)
+    e, d, f = 4, 256, 128
+    experts = rng.integers(0, e, 90).astype(np.int32)
+    rows = _bf16(rng.standard_normal((90, d)))
+    w = _weights(rng, e, d, f)
+    assert np.array_equal(_run(rows, experts, w), _run(rows, experts, w))
+    y = moe.moe_gather_swiglu(torch.empty((0, d), dtype=torch.bfloat16, device=DEV),
+                              torch.empty(0, dtype=torch.int32, device=DEV), *map(to_dev, w))
+    assert y.shape == (0, d)
+
+
+def test_decode_layer_with_experts_full_size():
+    """Decode with real experts: N=128, D=7168, E=256, top-8, unsorted identity
+    layout, F=2048.  Route + unsorted dispatch -> per-row SwiGLU reading the
+    rows where the dispatch left them -> combine.  Sampled rows of 8 experts
+    are checked against the oracle; the combine is checked on the GPU's own y
+    for 16 tokens."""
+    cfg = DECODE_FFN
+    inp = make_inputs(cfg)
+    w = make_swiglu_weights_device(cfg)
+    idx, tw, res = moe.moe_route_dispatch(to_dev(inp["logits"]), to_dev(inp["x"]), cfg.top_k,
+                                          cfg.n_segments, cfg.renormalize, cfg.sort, cfg.sort_cutoff)
+    assert not res.sorted
+    y = moe.moe_gather_swiglu(res.rows, res.row_expert, w["w_gate"], w["w_up"], w["w_down"])
+    out = moe.moe_combine(y, res.dst_pos, tw)
+    torch.cuda.synchronize()
+    rexp = to_np(res.row_expert)
+    assert np.array_equal(rexp, to_np(idx).reshape(-1))     # identity layout: row t*k+j
+    rng = np.random.default_rng(0)
+    chosen = np.sort(rng.choice(np.unique(rexp), 8, replace=False))
+    sample = np.nonzero(np.isin(rexp, chosen))[0]
+    sel = torch.from_numpy(chosen).to(DEV)
+    host = {k: v.index_select(0, sel).view(torch.int16).cpu().numpy().view(np.uint16)
+            for k, v in w.items()}
+    local = np.searchsorted(chosen, rexp[sample])
+    ref = swiglu_rows(to_np(res.rows)[sample], local, host["w_gate"], host["w_up"], host["w_down"])
+    check_swiglu(to_np(y)[sample], ref, local, what="decode experts")
+    yf = codecs.bf16_bits_to_f32(to_np(y))
+    toks = rng.choice(cfg.n_tokens, 16, replace=False)
+    exact = combine_f64(yf, to_np(res.dst_pos), to_np(tw), cfg.top_k, tokens=toks)
+    mag = combine_f64(np.abs(yf), to_np(res.dst_pos), np.abs(to_np(tw)), cfg.top_k, tokens=toks)
+    check_combine(to_np(out)[toks], exact, mag, True, what="decode combine")
+
+
+def test_gather_swiglu_multi_workgroup_grouping():
+    """300 experts (> 256) and 5000 rows (> 4096): the grouping of the ids
+    takes the multi-workgroup counting sort instead of the one-workgroup one."""
+    rng = np.random.default_rng(6)
+    e, d, f = 300, 128, 128
+    experts = rng.integers(0, e, 5000).astype(np.int32)
+    experts[:40] = 7                                   # one expert with three passes
+    rows = _bf16(rng.standard_normal((experts.size, d)))
+    w = _weights(rng, e, d, f)
+    got = _run(rows, experts, w)
+    check_swiglu(got, swiglu_rows(rows, experts, *w), experts, what="E=300 R=5000")

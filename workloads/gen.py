@@ -70,6 +70,14 @@ CONFIGS = {
 }
 
 
+# The decode workload with real experts behind it: the same tokens, logits and
+# unsorted layout, each of the 256 experts a SwiGLU FFN of a DeepSeek-V3-sized
+# routed expert (F = 2048; 88 MB of bf16 weights per expert, 22.5 GB in all).
+DECODE_FFN = replace(CONFIGS["decode"], name="decode_ffn", ffn=2048,
+                     note="N=128, D=7168 bf16, E=256, top-8, unsorted dispatch, "
+                          "SwiGLU experts F=2048 picked per row")
+
+
 def _children(seed: int):
     return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(4)]
 
