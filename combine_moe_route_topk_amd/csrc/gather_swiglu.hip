@@ -19,13 +19,20 @@
 // three [F, D] matrices per active expert against at most 16 rows.  Shape:
 //   * a pass is up to 16 rows of one expert, one 16-row tile of
 //     v_mfma_f32_16x16x32_bf16; an expert with more rows takes several passes;
-//   * a wave owns 64 weight rows over the whole K (gate/up: 32 F columns of
-//     W_gate and the same 32 of W_up, so h = silu(g) * u is lane-local; down:
-//     64 D columns) and streams them straight into registers, 128 K-elements
-//     per chunk with the next chunk in flight; no LDS, no barriers;
-//   * the 16 rows of a pass are read through L2, where each of the pass's
-//     column groups finds them; consecutive workgroups (one XCD) take the
-//     column groups of one pass.
+//   * a workgroup of 8 waves takes one pass and a group of columns; a wave
+//     owns 32 weight rows over the whole K (gate/up: 16 F columns of W_gate
+//     and the same 16 of W_up, so h = silu(g) * u is lane-local; down: 32 D
+//     columns) and streams them straight into registers, 512 K-elements of
+//     each weight row in flight;
+//   * the pass's 16 rows are staged through LDS 1024 K-elements at a time,
+//     double-buffered, one barrier per stage: each row byte is fetched once per
+//     workgroup instead of once per wave, which keeps the weight stream alone
+//     on the memory queues;
+//   * the pass count is only known on the device, so the grid is sized for the
+//     worst case; workgroup b runs on XCD b % 8 and XCD x takes passes
+//     x, x + 8, x + 16, ... (all column groups of one pass back to back, so its
+//     rows stay in that XCD's L2), which spreads the unused tail of the grid
+//     evenly over the XCDs.
 // Lane (n = l % 16, g = l / 16) holds row/column n and elements
 // [32 s + 8 g, +8) of MFMA step s; A and B use the same assignment, so each
 // step's 32-wide dot products cover their K slice exactly once.
@@ -38,41 +45,33 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPass = 16;           // rows per pass
-constexpr int kKC = 128;            // K elements per chunk
-constexpr int kSteps = kKC / 32;    // MFMA K steps per chunk
-constexpr int kNT = 4;              // 16-wide weight tiles per wave
-constexpr int kWaves = 4;           // waves per workgroup
+constexpr int kNT = 2;              // 16-wide weight tiles per wave
+constexpr int kWaves = 8;           // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
+constexpr int kSK = 1024;           // K elements per LDS stage
+constexpr int kPitch = kSK * 2 + 16;   // LDS row pitch: rows land 4 banks apart
+constexpr int kPieces = kPass * kSK / 8 / kThreads;   // 16-byte staging loads per thread
 constexpr int kXcds = 8;
 constexpr int kPlanThreads = 1024;  // one thread per expert (n_experts <= kMaxExperts)
 
 __device__ __forceinline__ float silu(float a) { return a / (1.f + expf(-a)); }
 
-struct Chunk {
-  bf16x8 a[kSteps];
-  bf16x8 b[kNT][kSteps];
+// One chunk (KC K-elements) of this lane's weight fragments: tile t, MFMA step s.
+template <int KC>
+struct BChunk {
+  bf16x8 b[kNT][KC / 32];
 };
 
-__device__ __forceinline__ void load_chunk(Chunk& ch, const uint16_t* a,
-                                           const uint16_t* const (&b)[kNT], int c) {
-  const int k0 = c * kKC;
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) ch.a[s] = *reinterpret_cast<const bf16x8*>(a + k0 + 32 * s);
+template <int KC>
+__device__ __forceinline__ void load_chunk(BChunk<KC>& ch, const uint16_t* const (&b)[kNT], int c) {
 #pragma unroll
   for (int t = 0; t < kNT; ++t)
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-      ch.b[t][s] = *reinterpret_cast<const bf16x8*>(b[t] + k0 + 32 * s);
-}
-
-__device__ __forceinline__ void mma(f32x4 (&acc)[kNT], const Chunk& ch) {
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s)
-#pragma unroll
-    for (int t = 0; t < kNT; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.a[s], ch.b[t][s], acc[t], 0, 0, 0);
+    for (int s = 0; s < KC / 32; ++s)
+      ch.b[t][s] = *reinterpret_cast<const bf16x8*>(b[t] + c * KC + 32 * s);
 }
 
 // Pass list from the expert offsets: expert e owns ceil(count_e / 16) passes;
@@ -113,43 +112,56 @@ __global__ __launch_bounds__(kPlanThreads) void gather_plan_kernel(
 //         C = h [R, F] in grouped order, h = bf16(silu(g) * u).
 // MODE 1: A = h [R, F] in grouped order, B = W_down [E, D, F],
 //         C = y [R, D] at the rows' own positions order[p].
-template <int MODE>
+// The weights stream in chunks of KC K-elements with DEPTH chunks in flight
+// (KC = 256, DEPTH = 2 when K is a multiple of 256, else 128 and 4: the same
+// bytes in flight and the same order of accumulation).
+template <int MODE, int KC, int DEPTH>
 __global__ __launch_bounds__(kThreads) void gather_gemm_kernel(
     const uint16_t* __restrict__ A, int K, const int32_t* __restrict__ order,
     const int4* __restrict__ passes, const int32_t* __restrict__ n_passes, int n_groups,
-    int n_tiles, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int NB,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int NB,
     uint16_t* __restrict__ C, int ldc) {
-  // XCD-aware placement: workgroup b runs on XCD b % 8; each XCD takes a
-  // contiguous range of tile ids, tile = pass * n_groups + column group
-  const int nb = gridDim.x;                 // a multiple of kXcds
+  __shared__ __align__(16) unsigned char sa[2][kPass * kPitch];
   const int b = blockIdx.x;
-  const int tile = (b % kXcds) * (nb / kXcds) + b / kXcds;
-  if (tile >= n_tiles) return;
-  const int pass = tile / n_groups, grp = tile % n_groups;
-  if (pass >= __builtin_amdgcn_readfirstlane(n_passes[0])) return;
+  const int slot = b / kXcds;
+  const int pass = (slot / n_groups) * kXcds + b % kXcds, grp = slot % n_groups;
+  if (pass >= __builtin_amdgcn_readfirstlane(n_passes[0])) return;   // whole workgroup
   const int4 ps = passes[pass];
   const int expert = __builtin_amdgcn_readfirstlane(ps.x);
   const int row0 = __builtin_amdgcn_readfirstlane(ps.y);
   const int row_end = __builtin_amdgcn_readfirstlane(ps.z);
 
+  const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = lane & 15, g = lane >> 4;
-  constexpr int kCols = MODE == 0 ? 32 : 64;           // output columns per wave
+  constexpr int kCols = MODE == 0 ? kNT * 8 : kNT * 16;   // output columns per wave
   const int col0 = (grp * kWaves + w) * kCols;
-  if (col0 >= NB) return;                               // past the last column; no barriers follow
+  // a wave past the last column still stages rows and meets every barrier
+  const bool active = col0 < NB;
 
-  // rows past the end of the pass repeat its first row; they are never stored
-  const int p = row0 + n < row_end ? row0 + n : row0;
-  const int64_t arow = MODE == 0 ? int64_t(order[p]) : int64_t(p);
-  const uint16_t* a_ptr = A + arow * K + 8 * g;
+  // staging: piece q = tid + kThreads * j is row q / (kSK / 8), 16-byte column
+  // q % (kSK / 8) of the stage; rows past the end of the pass repeat its first
+  // row (never stored)
+  const uint16_t* a_src[kPieces];
+  int a_lds[kPieces], a_col[kPieces];
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) {
+    const int q = tid + kThreads * j;
+    const int row = q / (kSK / 8);
+    a_col[j] = 8 * (q % (kSK / 8));
+    const int p = row0 + row < row_end ? row0 + row : row0;
+    const int64_t arow = MODE == 0 ? int64_t(order[p]) : int64_t(p);
+    a_src[j] = A + arow * K + a_col[j];
+    a_lds[j] = row * kPitch + 2 * a_col[j];
+  }
   const uint16_t* b_ptr[kNT];
 #pragma unroll
   for (int t = 0; t < kNT; ++t) {
-    // gate/up: tiles 0, 1 = gate columns col0 + 16t, tiles 2, 3 = the same columns of up
-    int col = MODE == 0 ? col0 + 16 * (t & 1) + n : col0 + 16 * t + n;
+    // gate/up: tile 0 = gate columns, tile 1 = the same columns of up
+    int col = MODE == 0 ? col0 + n : col0 + 16 * t + n;
     if (col >= NB) col = NB - 1;                        // partial last group; never stored
-    const uint16_t* base = (MODE == 0 && t >= 2) ? B1 : B0;
+    const uint16_t* base = (MODE == 0 && t == 1) ? B1 : B0;
     b_ptr[t] = base + (int64_t(expert) * NB + col) * K + 8 * g;
   }
 
@@ -157,29 +169,58 @@ __global__ __launch_bounds__(kThreads) void gather_gemm_kernel(
 #pragma unroll
   for (int t = 0; t < kNT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // two chunks in registers: chunk c is multiplied while chunk c + 1 loads
-  const int nc = K / kKC;
-  Chunk c0, c1;
-  load_chunk(c0, a_ptr, b_ptr, 0);
-  if (nc > 1) load_chunk(c1, a_ptr, b_ptr, 1);
-  int c = 0;
-  for (; c + 3 < nc; c += 2) {
-    mma(acc, c0);
-    load_chunk(c0, a_ptr, b_ptr, c + 2);
-    mma(acc, c1);
-    load_chunk(c1, a_ptr, b_ptr, c + 3);
+  constexpr int kCPS = kSK / KC;                        // chunks per stage, a multiple of DEPTH
+  const int nc = K / KC;
+  const int n_st = (K + kSK - 1) / kSK;
+  BChunk<KC> ring[DEPTH];                               // chunk c lives in ring[c % DEPTH]
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < DEPTH; ++r)
+      if (r < nc) load_chunk(ring[r], b_ptr, r);
   }
-  if (c + 2 < nc) {                                     // three chunks left
-    mma(acc, c0);
-    load_chunk(c0, a_ptr, b_ptr, c + 2);
-    mma(acc, c1);
-    mma(acc, c0);
-  } else if (c + 1 < nc) {                              // two left
-    mma(acc, c0);
-    mma(acc, c1);
-  } else {
-    mma(acc, c0);
+  u32x4 stg[kPieces];
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j)
+    if (a_col[j] < K) stg[j] = *reinterpret_cast<const u32x4*>(a_src[j]);
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j)
+    if (a_col[j] < K) *reinterpret_cast<u32x4*>(&sa[0][a_lds[j]]) = stg[j];
+  __syncthreads();
+
+  for (int st = 0; st < n_st; ++st) {
+    const int k1 = (st + 1) * kSK;                      // first element of the next stage
+    if (k1 < K) {
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j)
+        if (k1 + a_col[j] < K) stg[j] = *reinterpret_cast<const u32x4*>(a_src[j] + k1);
+    }
+    if (active) {
+      const unsigned char* arow = sa[st & 1] + n * kPitch + 16 * g;
+#pragma unroll
+      for (int cc = 0; cc < kCPS; ++cc) {
+        const int c = st * kCPS + cc;
+        if (c < nc) {                                   // partial last stage (uniform)
+          BChunk<KC>& ch = ring[cc % DEPTH];
+#pragma unroll
+          for (int s = 0; s < KC / 32; ++s) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + (cc * KC + 32 * s) * 2);
+#pragma unroll
+            for (int t = 0; t < kNT; ++t)
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ch.b[t][s], acc[t], 0, 0, 0);
+          }
+          if (c + DEPTH < nc) load_chunk(ch, b_ptr, c + DEPTH);
+        }
+      }
+    }
+    if (k1 < K) {
+      // the other buffer was last read in stage st - 1, which every wave has left
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j)
+        if (k1 + a_col[j] < K) *reinterpret_cast<u32x4*>(&sa[(st + 1) & 1][a_lds[j]]) = stg[j];
+    }
+    __syncthreads();
   }
+  if (!active) return;
 
   // lane holds C[4 g + i][n] of each 16 x 16 tile
 #pragma unroll
@@ -187,12 +228,8 @@ __global__ __launch_bounds__(kThreads) void gather_gemm_kernel(
     const int pr = row0 + 4 * g + i;
     if (pr >= row_end) continue;
     if (MODE == 0) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int col = col0 + 16 * hh + n;
-        if (col < NB)
-          C[int64_t(pr) * ldc + col] = f32_to_bf16_rne(silu(acc[hh][i]) * acc[2 + hh][i]);
-      }
+      const int col = col0 + n;
+      if (col < NB) C[int64_t(pr) * ldc + col] = f32_to_bf16_rne(silu(acc[0][i]) * acc[1][i]);
     } else {
       const int64_t dst = order[pr];
 #pragma unroll
@@ -236,11 +273,19 @@ size_t gather_swiglu_workspace_bytes(int64_t n_rows, int n_experts, int64_t hidd
   return gather_layout(n_rows, n_experts, ffn).total;
 }
 
+namespace {
+// column groups of the two products and the worst-case pass count, rounded up
+// to a multiple of the XCD count
+int64_t groups_gate_up(int64_t ffn) { return (ffn + kWaves * kNT * 8 - 1) / (kWaves * kNT * 8); }
+int64_t groups_down(int64_t hidden) { return (hidden + kWaves * kNT * 16 - 1) / (kWaves * kNT * 16); }
+int64_t pass_slots(int64_t n_rows, int n_experts) {
+  return ((n_rows + kPass - 1) / kPass + n_experts + kXcds - 1) / kXcds * kXcds;
+}
+}  // namespace
+
 int64_t gather_swiglu_tiles(int64_t n_rows, int n_experts, int64_t hidden, int64_t ffn) {
-  const int64_t passes = (n_rows + kPass - 1) / kPass + n_experts;
-  const int64_t g1 = (ffn + kWaves * 32 - 1) / (kWaves * 32);
-  const int64_t g2 = (hidden + kWaves * 64 - 1) / (kWaves * 64);
-  return passes * (g1 > g2 ? g1 : g2);
+  const int64_t g1 = groups_gate_up(ffn), g2 = groups_down(hidden);
+  return pass_slots(n_rows, n_experts) * (g1 > g2 ? g1 : g2);
 }
 
 hipError_t launch_gather_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
@@ -277,22 +322,32 @@ hipError_t launch_gather_swiglu(const void* rows, int64_t n_rows, int64_t hidden
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-  auto grid_for = [](int64_t tiles) { return unsigned((tiles + kXcds - 1) / kXcds * kXcds); };
+  const int64_t slots = pass_slots(n_rows, n_experts);
   // 3. gate/up: 128 F columns per workgroup, K = D
-  const int g1 = int((ffn + kWaves * 32 - 1) / (kWaves * 32));
-  const int64_t t1 = int64_t(L.max_passes) * g1;
-  gather_gemm_kernel<0><<<grid_for(t1), kThreads, 0, stream>>>(
-      static_cast<const uint16_t*>(rows), int(hidden), order, passes, n_passes, g1, int(t1),
-      static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), int(ffn), h,
-      int(ffn));
+  const int g1 = int(groups_gate_up(ffn));
+  const dim3 grid1(unsigned(slots * g1));
+  const uint16_t* r16 = static_cast<const uint16_t*>(rows);
+  const uint16_t* wg = static_cast<const uint16_t*>(w_gate);
+  const uint16_t* wu = static_cast<const uint16_t*>(w_up);
+  if (hidden % 256 == 0)
+    gather_gemm_kernel<0, 256, 2><<<grid1, kThreads, 0, stream>>>(
+        r16, int(hidden), order, passes, n_passes, g1, wg, wu, int(ffn), h, int(ffn));
+  else
+    gather_gemm_kernel<0, 128, 4><<<grid1, kThreads, 0, stream>>>(
+        r16, int(hidden), order, passes, n_passes, g1, wg, wu, int(ffn), h, int(ffn));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   // 4. down: 256 D columns per workgroup, K = F
-  const int g2 = int((hidden + kWaves * 64 - 1) / (kWaves * 64));
-  const int64_t t2 = int64_t(L.max_passes) * g2;
-  gather_gemm_kernel<1><<<grid_for(t2), kThreads, 0, stream>>>(
-      h, int(ffn), order, passes, n_passes, g2, int(t2), static_cast<const uint16_t*>(w_down),
-      nullptr, int(hidden), static_cast<uint16_t*>(y), int(hidden));
+  const int g2 = int(groups_down(hidden));
+  const dim3 grid2(unsigned(slots * g2));
+  const uint16_t* wd = static_cast<const uint16_t*>(w_down);
+  uint16_t* y16 = static_cast<uint16_t*>(y);
+  if (ffn % 256 == 0)
+    gather_gemm_kernel<1, 256, 2><<<grid2, kThreads, 0, stream>>>(
+        h, int(ffn), order, passes, n_passes, g2, wd, nullptr, int(hidden), y16, int(hidden));
+  else
+    gather_gemm_kernel<1, 128, 4><<<grid2, kThreads, 0, stream>>>(
+        h, int(ffn), order, passes, n_passes, g2, wd, nullptr, int(hidden), y16, int(hidden));
   return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ def _run(rows, experts, w, y=None):
     (2, 640, 128, [20, 4]),                    # five chunks; down has one chunk (K = 128)
     (16, 128, 512, [1] * 16),                  # one row per expert, partial down group
     (1, 512, 256, [70]),                       # a single expert, five passes
+    (2, 2432, 1152, [20, 3]),                  # K not a multiple of the 1024-wide row stage
 ])
 def test_gather_swiglu_small(e, d, f, counts):
     rng = np.random.default_rng(d + 7 * f + e)
