@@ -404,7 +404,7 @@ int moe_grouped_gemm_fp8(const void* rows, const float* row_scales, int64_t n_ro
     return fail(MOE_ERR_UNSUPPORTED, "%s: k_dim and n_dim must be multiples of 128", fn);
   if (n_rows > INT32_MAX || n_dim > INT32_MAX || k_dim > INT32_MAX)
     return fail(MOE_ERR_UNSUPPORTED, "%s: sizes exceed the int32 range", fn);
-  const int64_t tiles = ((n_rows + 63) / 64 + n_experts) * (n_dim / 128);
+  const int64_t tiles = ((n_rows + 63) / 64 + n_experts + 7) / 8 * 8 * (n_dim / 128);
   if (tiles > INT32_MAX - 8) return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", fn);
   if (n_rows == 0) return ok();
   if (!rows || !row_scales || !expert_offsets || !w || !w_scales || !y)

@@ -243,11 +243,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_kernel(
     int n_tiles) {
   __shared__ __align__(1024) unsigned char ring[NS * kSlotBytes];
 
-  const int nb = gridDim.x;                 // a multiple of kXcds
+  // workgroup b runs on XCD b % 8; XCD x takes row tiles x, x + 8, ..., each
+  // with all its column tiles back to back (the tile's rows stay in that XCD's
+  // L2).  The grid covers the worst-case row-tile count; interleaving the row
+  // tiles over the XCDs spreads the unused ones evenly.
   const int b = blockIdx.x;
-  const int tile = (b % kXcds) * (nb / kXcds) + b / kXcds;
-  if (int64_t(tile) >= int64_t(max_m_tiles) * n_tiles) return;
-  const int m_idx = tile / n_tiles, n_tile = tile % n_tiles;
+  const int slot = b / kXcds;
+  const int m_idx = (slot / n_tiles) * kXcds + b % kXcds, n_tile = slot % n_tiles;
+  if (m_idx >= max_m_tiles) return;
   Fp8Tile ti = find_fp8_tile(m_idx, offs, n_experts, n_rows);
   if (!ti.valid) return;
   // the lookup's results are wave-uniform; saying so keeps the tile's
@@ -322,8 +325,8 @@ hipError_t launch_grouped_gemm_fp8(const void* rows, const float* row_scales, in
                                    hipStream_t stream) {
   const int max_m_tiles = int((n_rows + kTM - 1) / kTM) + n_experts;
   const int n_tiles = int(n_dim / kTN);
-  const int64_t tiles = int64_t(max_m_tiles) * n_tiles;
-  const unsigned grid = unsigned((tiles + kXcds - 1) / kXcds * kXcds);
+  const int64_t m_slots = (int64_t(max_m_tiles) + kXcds - 1) / kXcds * kXcds;
+  const unsigned grid = unsigned(m_slots * n_tiles);
   grouped_gemm_fp8_kernel<kRingSlots><<<grid, kThreads, 0, stream>>>(
       static_cast<const uint8_t*>(rows), row_scales, n_rows, int(k_dim), expert_offsets,
       n_experts, static_cast<const uint8_t*>(w), w_scales, int(n_dim),
