@@ -19,10 +19,24 @@ expert's activation.
 Arithmetic: float64 on the bf16-valued inputs, h and y rounded once to bf16
 (correct rounding from float64).
 
+The same function serves rows in any order, each with its own expert: the
+per-row expert ids of gather_mm on the unsorted decode layout ("backends/mlx:
+runtime MoE expert-sort for decode (issue #20554)", Summary), and the batched
+expert FFN planned for decode in "MLX expert parallelism all_to_all PR 3158"
+(Facts list).
+
+swiglu_combine is the weighted top-k sum taken straight from the FFN result,
+the zero-copy combine that the same MLX PR planned (Facts list): out[t] =
+out0[t] + sum_j w_tj * y(t, j), with y never rounded to bf16 -- our reading of
+a combine fused into the down product, whose accumulator is fp32.
+
 Pins (tests/test_oracle_swiglu.py): a pure-Python brute force (math.fsum dot
 products) on a tiny case; silu closed forms (silu(0) = 0, odd-part identity
 silu(a) - silu(-a) = a); layout invariance -- the output for pair (t, j) does
-not depend on where dispatch put its row; empty experts produce no rows.
+not depend on where dispatch put its row; empty experts produce no rows; the
+fused combine against a pure-Python brute force (pairs looked up by scanning
+the rows), its k = 1 / unit-weight special case, and its invariance under a
+shuffle of the rows.
 """
 from __future__ import annotations
 
@@ -38,17 +52,18 @@ def silu(a: np.ndarray) -> np.ndarray:
     return a / (1.0 + np.exp(-a))
 
 
-def swiglu_rows(rows_bf16: np.ndarray, experts: np.ndarray, w_gate_bf16, w_up_bf16,
-                w_down_bf16) -> np.ndarray:
-    """Evaluate the expert FFN on selected rows.
-
-    rows_bf16 uint16 [M, D]; experts int [M]; weights uint16 bit patterns
-    (indexable by expert: [E, F, D], [E, F, D], [E, D, F]).  Returns y as
-    uint16 bf16 bit patterns [M, D]."""
+def swiglu_rows_f64(rows_bf16: np.ndarray, experts: np.ndarray, w_gate_bf16, w_up_bf16,
+                    w_down_bf16) -> np.ndarray:
+    """float64 [M, D] value of y before its final rounding (h is rounded to
+    bf16 as in the definition).  Rows whose expert lies outside [0, E) give 0
+    (they take no part)."""
     r = bf16_bits_to_f32(rows_bf16).astype(np.float64)
     experts = np.asarray(experts, dtype=np.int64)
-    out = np.empty(r.shape, dtype=np.uint16)
+    n_exp = np.asarray(w_gate_bf16).shape[0]
+    out = np.zeros(r.shape, dtype=np.float64)
     for e in np.unique(experts):
+        if e < 0 or e >= n_exp:
+            continue
         sel = np.nonzero(experts == e)[0]
         wg = bf16_bits_to_f32(w_gate_bf16[e]).astype(np.float64)
         wu = bf16_bits_to_f32(w_up_bf16[e]).astype(np.float64)
@@ -56,7 +71,41 @@ def swiglu_rows(rows_bf16: np.ndarray, experts: np.ndarray, w_gate_bf16, w_up_bf
         x = r[sel]
         h_bits = f64_to_bf16_bits(silu(x @ wg.T) * (x @ wu.T))
         h = bf16_bits_to_f32(h_bits).astype(np.float64)
-        out[sel] = f64_to_bf16_bits(h @ wd.T)
+        out[sel] = h @ wd.T
+    return out
+
+
+def swiglu_rows(rows_bf16: np.ndarray, experts: np.ndarray, w_gate_bf16, w_up_bf16,
+                w_down_bf16) -> np.ndarray:
+    """Evaluate the expert FFN on selected rows.
+
+    rows_bf16 uint16 [M, D]; experts int [M]; weights uint16 bit patterns
+    (indexable by expert: [E, F, D], [E, F, D], [E, D, F]).  Returns y as
+    uint16 bf16 bit patterns [M, D]."""
+    return f64_to_bf16_bits(swiglu_rows_f64(rows_bf16, experts, w_gate_bf16, w_up_bf16,
+                                            w_down_bf16))
+
+
+def swiglu_combine(rows_bf16, experts, row_pair, topk_w, k: int, w_gate_bf16, w_up_bf16,
+                   w_down_bf16, out0=None) -> np.ndarray:
+    """The combine fused into the expert FFN (zero-copy combine): for every
+    token t,
+
+        out[t] = out0[t] + sum_j topk_w[t, j] * y(t, j)
+
+    where y(t, j) is the FFN output, before any rounding of y, of the row r
+    holding pair q = t*k + j (row_pair[r] == q) computed with expert
+    experts[r].  Rows with an expert outside [0, E) add nothing.  float64
+    [N, D]; N = len(topk_w) // k (topk_w flattened over [N, k])."""
+    w = np.asarray(topk_w, dtype=np.float32).astype(np.float64).reshape(-1)
+    n_tok = w.size // k
+    y = swiglu_rows_f64(rows_bf16, experts, w_gate_bf16, w_up_bf16, w_down_bf16)
+    out = np.zeros((n_tok, y.shape[1]), dtype=np.float64)
+    if out0 is not None:
+        out += np.asarray(out0, dtype=np.float64)
+    q = np.asarray(row_pair, dtype=np.int64)
+    for r in range(q.size):           # each row adds its term to its token
+        out[q[r] // k] += w[q[r]] * y[r]
     return out
 
 

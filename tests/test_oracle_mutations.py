@@ -159,6 +159,39 @@ def test_swiglu_pins_catch_sigmoid_for_silu(monkeypatch):
     _fails(tsw.test_rows_match_pure_python_brute_force)
 
 
+def _fused_mutant(kind):
+    """Mutants of the fused combine: the weight of the transposed slot, the
+    token taken as q % N instead of q // k, or y rounded to bf16 first."""
+    def f(rows, experts, row_pair, topk_w, k, wg, wu, wd, out0=None):
+        w = np.asarray(topk_w, np.float32).astype(np.float64).reshape(-1)
+        n_tok = w.size // k
+        y = osw.swiglu_rows_f64(rows, experts, wg, wu, wd)
+        if kind == "round_y":
+            y = codecs.bf16_bits_to_f32(codecs.f64_to_bf16_bits(y)).astype(np.float64)
+        out = np.zeros((n_tok, y.shape[1])) + (0 if out0 is None else np.asarray(out0, np.float64))
+        for r, q in enumerate(np.asarray(row_pair, np.int64)):
+            t = q % n_tok if kind == "token_mod" else q // k
+            wq = w.reshape(n_tok, k)[t, (q % k + 1) % k] if kind == "slot" else w[q]
+            out[t] += wq * y[r]
+        return out
+    return f
+
+
+@pytest.mark.parametrize("kind", ["slot", "token_mod", "round_y"])
+def test_fused_combine_pins_catch(monkeypatch, kind):
+    monkeypatch.setattr(tsw, "swiglu_combine", _fused_mutant(kind))
+    results = []
+    for t in (tsw.test_fused_combine_matches_pure_python_brute_force,
+              tsw.test_fused_combine_k1_unit_weights_is_the_unrounded_ffn,
+              tsw.test_fused_combine_invariant_under_row_shuffle_and_skips_bad_ids):
+        try:
+            t()
+            results.append(False)
+        except AssertionError:
+            results.append(True)
+    assert any(results), f"no fused-combine pin caught the {kind} mutant"
+
+
 # ------------------------------------------------------------------ fp8 grouped GEMM mutants
 
 from oracle import gemm_fp8 as og

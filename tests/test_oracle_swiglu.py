@@ -1,8 +1,11 @@
 """Pins for the grouped SwiGLU oracle (CPU only)."""
+import math
+
 import numpy as np
 
 from oracle import codecs, dispatch as od
-from oracle.swiglu import grouped_swiglu, silu, swiglu_brute, swiglu_rows
+from oracle.swiglu import (grouped_swiglu, silu, swiglu_brute, swiglu_combine, swiglu_rows,
+                           swiglu_rows_f64)
 
 
 def _bf16(a):
@@ -64,3 +67,61 @@ def test_layout_invariance():
         y = swiglu_rows(rows, rexp, wg, wu, wd)
         per_pair[sorted_] = y[dst]          # back to pair order
     assert np.array_equal(per_pair[True], per_pair[False])
+
+
+def _fused_case(seed=3, n=5, k=3, e=4, d=6, f=7):
+    rng = np.random.default_rng(seed)
+    wg, wu = _bf16(rng.standard_normal((e, f, d)) * 0.4), _bf16(rng.standard_normal((e, f, d)) * 0.4)
+    wd = _bf16(rng.standard_normal((e, d, f)) * 0.4)
+    rows = _bf16(rng.standard_normal((n * k, d)))
+    experts = rng.integers(0, e, n * k)
+    row_pair = rng.permutation(n * k)                   # rows in a shuffled layout
+    tw = rng.uniform(0.05, 1.0, (n, k)).astype(np.float32)
+    return rows, experts, row_pair, tw, k, (wg, wu, wd)
+
+
+def test_fused_combine_matches_pure_python_brute_force():
+    rows, experts, row_pair, tw, k, w = _fused_case()
+    out0 = np.arange(5 * 6, dtype=np.float64).reshape(5, 6) * 0.25
+    got = swiglu_combine(rows, experts, row_pair, tw, k, *w, out0=out0)
+    dec = lambda b: codecs.bf16_bits_to_f32(b).astype(np.float64).tolist()
+    n = tw.shape[0]
+    for t in range(n):
+        for i in range(6):
+            terms = [out0[t, i]]
+            for j in range(k):
+                r = [rr for rr in range(len(row_pair)) if row_pair[rr] == t * k + j][0]
+                ex = experts[r]
+                y = swiglu_brute(dec(rows[r]), dec(w[0][ex]), dec(w[1][ex]), dec(w[2][ex]))
+                terms.append(float(tw[t, j]) * y[i])
+            ref = math.fsum(terms)
+            # h is rounded to bf16 on both sides (a tie-side flip moves y by far
+            # less than this); the sums are otherwise exact up to float64
+            assert abs(got[t, i] - ref) <= 1e-3 * math.fsum(abs(v) for v in terms) + 1e-12, (t, i)
+
+
+def test_fused_combine_k1_unit_weights_is_the_unrounded_ffn():
+    rng = np.random.default_rng(4)
+    e, d, f, n = 3, 5, 4, 6
+    wg, wu = _bf16(rng.standard_normal((e, f, d))), _bf16(rng.standard_normal((e, f, d)))
+    wd = _bf16(rng.standard_normal((e, d, f)))
+    rows = _bf16(rng.standard_normal((n, d)))
+    experts = rng.integers(0, e, n)
+    got = swiglu_combine(rows, experts, np.arange(n), np.ones((n, 1), np.float32), 1, wg, wu, wd)
+    assert np.array_equal(got, swiglu_rows_f64(rows, experts, wg, wu, wd))
+    # and rounding it gives the rounded FFN rows
+    assert np.array_equal(codecs.f64_to_bf16_bits(got), swiglu_rows(rows, experts, wg, wu, wd))
+
+
+def test_fused_combine_invariant_under_row_shuffle_and_skips_bad_ids():
+    rows, experts, row_pair, tw, k, w = _fused_case(seed=5)
+    a = swiglu_combine(rows, experts, row_pair, tw, k, *w)
+    perm = np.random.default_rng(6).permutation(len(row_pair))
+    b = swiglu_combine(rows[perm], experts[perm], row_pair[perm], tw, k, *w)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
+    bad = experts.copy()
+    bad[0] = 99                                          # this row takes no part
+    c = swiglu_combine(rows, bad, row_pair, tw, k, *w)
+    t0 = row_pair[0] // k
+    others = np.arange(tw.shape[0]) != t0
+    assert np.array_equal(c[others], a[others]) and not np.allclose(c[t0], a[t0])
