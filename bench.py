@@ -398,8 +398,18 @@ def time_gather_swiglu(torch, moe, steps=10, warmup=2, cpu=False):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
+    out32 = torch.empty((cfg.n_tokens, d), dtype=torch.float32, device=dev)
+
+    def layer_fused():
+        moe.moe_route_dispatch(logits, x, cfg.top_k, cfg.n_segments, cfg.renormalize, cfg.sort,
+                               cfg.sort_cutoff, topk_idx=idx, topk_w=tw, workspace=rd_ws, out=res)
+        out32.zero_()
+        moe.moe_gather_swiglu_combine(res.rows, res.row_expert, tw, w["w_gate"], w["w_up"],
+                                      w["w_down"], row_pair=res.src_pair, out=out32, workspace=ws)
+
     ms = timed(ffn)
     ms_layer = timed(layer)
+    ms_fused = timed(layer_fused)
     counts = res.expert_counts.cpu().numpy()
     active = int((counts > 0).sum())
     wbytes = active * 3 * f * d * 2
@@ -411,10 +421,13 @@ def time_gather_swiglu(torch, moe, steps=10, warmup=2, cpu=False):
            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
            "layer_ms": round(ms_layer, 3),
            "layer_calls": "moe_route_dispatch (unsorted, with rows) + moe_gather_swiglu + moe_combine",
+           "layer_fused_ms": round(ms_fused, 3),
+           "layer_fused_calls": "moe_route_dispatch + zero fill of the fp32 out + "
+                                "moe_gather_swiglu_combine (combine fused into the down product)",
            "bound": "hbm (weights)", "dtype": "bf16 in, fp32 accumulate, bf16 out"}
     if cpu:
         rec["cpu_oracle"] = cpu_oracle_gather_swiglu(torch, res, w)
-    del w, y, ws, res, x, logits
+    del w, y, ws, res, x, logits, out32
     torch.cuda.empty_cache()
     return rec
 

@@ -46,6 +46,8 @@ SIGNATURES = {
     "moe_gather_swiglu_workspace_bytes": (_sz, [_i64, _i32, _i64, _i64]),
     "moe_gather_swiglu": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _p, _i64, _p, _p,
                                          _sz, _p]),
+    "moe_gather_swiglu_combine": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _i64, _i32, _i32, _p,
+                                                 _p, _p, _i64, _p, _p, _sz, _p]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _i32, _p, _p, _i64, _p, _p]),
 }
 

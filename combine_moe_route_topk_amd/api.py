@@ -326,6 +326,45 @@ def moe_gather_swiglu(rows: torch.Tensor, row_expert: torch.Tensor, w_gate: torc
     return y
 
 
+def moe_gather_swiglu_combine(rows: torch.Tensor, row_expert: torch.Tensor,
+                              topk_w: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+                              w_down: torch.Tensor, row_pair: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_gather_swiglu with the combine fused in: out [N, D] float32 (zeros
+    unless given) += sum over rows r of topk_w[q] * FFN(rows[r]) at token q // k,
+    q = row_pair[r] (or r); topk_w [N, k] float32."""
+    _need(rows, "rows", (torch.bfloat16,))
+    dev = rows.device
+    for name, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, name, (torch.bfloat16,), dev)
+    _need(row_expert, "row_expert", (torch.int32,), dev)
+    _need(topk_w, "topk_w", (torch.float32,), dev)
+    r, d = rows.shape
+    e, f, d2 = w_gate.shape
+    n, k = topk_w.shape
+    if d2 != d or tuple(w_up.shape) != (e, f, d) or tuple(w_down.shape) != (e, d, f) or \
+            row_expert.numel() != r:
+        raise ValueError("moe_gather_swiglu_combine: inconsistent shapes")
+    if row_pair is not None:
+        _need(row_pair, "row_pair", (torch.int32,), dev)
+        if row_pair.numel() != r:
+            raise ValueError("moe_gather_swiglu_combine: row_pair must have one entry per row")
+    if out is None:
+        out = torch.zeros((n, d), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), dev)
+    if tuple(out.shape) != (n, d):
+        raise ValueError("moe_gather_swiglu_combine: out must be [N, D]")
+    if workspace is None:
+        workspace = torch.empty(max(moe_gather_swiglu_workspace_bytes(r, e, d, f), 256),
+                                dtype=torch.uint8, device=dev)
+    check("moe_gather_swiglu_combine", lib.moe_gather_swiglu_combine(
+        _ptr(rows), r, d, _ptr(row_expert), _ptr(row_pair) if row_pair is not None else None,
+        _ptr(topk_w), n, k, e, _ptr(w_gate), _ptr(w_up), _ptr(w_down), f, _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
 def moe_grouped_gemm_fp8(rows: torch.Tensor, row_scales: torch.Tensor, expert_offsets: torch.Tensor,
                          w: torch.Tensor, w_scales: torch.Tensor, y: Optional[torch.Tensor] = None,
                          stream=None) -> torch.Tensor:

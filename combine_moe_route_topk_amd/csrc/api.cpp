@@ -392,6 +392,44 @@ int moe_gather_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                     fn);
 }
 
+int moe_gather_swiglu_combine(const void* rows, int64_t n_rows, int64_t hidden,
+                              const int32_t* row_expert, const int32_t* row_pair,
+                              const float* topk_w, int64_t n_tokens, int32_t k, int32_t n_experts,
+                              const void* w_gate, const void* w_up, const void* w_down,
+                              int64_t ffn, float* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  const char* fn = "moe_gather_swiglu_combine";
+  if (n_rows < 0 || n_tokens < 0) return fail(MOE_ERR_ARG, "%s: n_rows and n_tokens must be >= 0", fn);
+  if (hidden < 1 || ffn < 1 || n_experts < 1) return fail(MOE_ERR_ARG, "%s: sizes must be >= 1", fn);
+  if (k < 1 || k > moe::kMaxTopK) return fail(MOE_ERR_ARG, "%s: k must be in [1, %d]", fn, moe::kMaxTopK);
+  if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "%s: n_experts > %d", fn, MOE_MAX_EXPERTS);
+  if (hidden % 128 != 0 || ffn % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: hidden and ffn must be multiples of 128", fn);
+  if (n_rows > INT32_MAX || hidden > INT32_MAX || ffn > INT32_MAX || n_tokens * k > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: sizes exceed the int32 range", fn);
+  if (moe::gather_swiglu_tiles(n_rows, n_experts, hidden, ffn) > INT32_MAX - 8)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  if (n_rows == 0 || n_tokens == 0) return ok();
+  if (!rows || !row_expert || !topk_w || !w_gate || !w_up || !w_down || !out)
+    return fail(MOE_ERR_ARG, "%s: null pointer argument", fn);
+  if ((reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(w_gate) |
+       reinterpret_cast<uintptr_t>(w_up) | reinterpret_cast<uintptr_t>(w_down)) & 15)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: rows and weights must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(topk_w)) & 3)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: out and topk_w must be 4-byte aligned", fn);
+  const size_t need = moe::gather_swiglu_workspace_bytes(n_rows, n_experts, hidden, ffn);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : size_t(0));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  const moe::FusedCombine fc{row_pair, topk_w, out, int(k), int(n_tokens * k)};
+  return hip_status(moe::launch_gather_swiglu(rows, n_rows, hidden, row_expert, n_experts,
+                                              w_gate, w_up, w_down, ffn, nullptr, workspace,
+                                              static_cast<hipStream_t>(stream), &fc),
+                    fn);
+}
+
 int moe_grouped_gemm_fp8(const void* rows, const float* row_scales, int64_t n_rows,
                          int64_t k_dim, const int32_t* expert_offsets, int32_t n_experts,
                          const void* w, const float* w_scales, int64_t n_dim, void* y,

@@ -112,6 +112,9 @@ __global__ __launch_bounds__(kPlanThreads) void gather_plan_kernel(
 //         C = h [R, F] in grouped order, h = bf16(silu(g) * u).
 // MODE 1: A = h [R, F] in grouped order, B = W_down [E, D, F],
 //         C = y [R, D] at the rows' own positions order[p].
+// MODE 2: as MODE 1, but y is not stored: the fp32 result of row r, which
+//         holds pair q = fc.row_pair[r] (q = r without the map), is weighted
+//         by topk_w[q] and added into out[q / k] (the combine, fused).
 // The weights stream in chunks of KC K-elements with DEPTH chunks in flight
 // (KC = 256, DEPTH = 2 when K is a multiple of 256, else 128 and 4: the same
 // bytes in flight and the same order of accumulation).
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void gather_gemm_kernel(
     const uint16_t* __restrict__ A, int K, const int32_t* __restrict__ order,
     const int4* __restrict__ passes, const int32_t* __restrict__ n_passes, int n_groups,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int NB,
-    uint16_t* __restrict__ C, int ldc) {
+    uint16_t* __restrict__ C, int ldc, FusedCombine fc) {
   __shared__ __align__(16) unsigned char sa[2][kPass * kPitch];
   const int b = blockIdx.x;
   const int slot = b / kXcds;
@@ -230,12 +233,23 @@ __global__ __launch_bounds__(kThreads) void gather_gemm_kernel(
     if (MODE == 0) {
       const int col = col0 + n;
       if (col < NB) C[int64_t(pr) * ldc + col] = f32_to_bf16_rne(silu(acc[0][i]) * acc[1][i]);
-    } else {
+    } else if (MODE == 1) {
       const int64_t dst = order[pr];
 #pragma unroll
       for (int t = 0; t < kNT; ++t) {
         const int col = col0 + 16 * t + n;
         if (col < NB) C[dst * ldc + col] = f32_to_bf16_rne(acc[t][i]);
+      }
+    } else {
+      const int r = order[pr];
+      const int q = fc.row_pair ? fc.row_pair[r] : r;
+      if (unsigned(q) >= unsigned(fc.n_pairs)) continue;   // a row that holds no pair
+      const float wq = fc.topk_w[q];
+      float* o = fc.out + int64_t(q / fc.k) * ldc;
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) {
+        const int col = col0 + 16 * t + n;
+        if (col < NB) unsafeAtomicAdd(o + col, wq * acc[t][i]);
       }
     }
   }
@@ -291,7 +305,7 @@ int64_t gather_swiglu_tiles(int64_t n_rows, int n_experts, int64_t hidden, int64
 hipError_t launch_gather_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                                 const int32_t* row_expert, int n_experts, const void* w_gate,
                                 const void* w_up, const void* w_down, int64_t ffn, void* y,
-                                void* workspace, hipStream_t stream) {
+                                void* workspace, hipStream_t stream, const FusedCombine* fused) {
   const GatherLayout L = gather_layout(n_rows, n_experts, ffn);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
@@ -323,6 +337,7 @@ hipError_t launch_gather_swiglu(const void* rows, int64_t n_rows, int64_t hidden
   if (err != hipSuccess) return err;
 
   const int64_t slots = pass_slots(n_rows, n_experts);
+  const FusedCombine none{};
   // 3. gate/up: 128 F columns per workgroup, K = D
   const int g1 = int(groups_gate_up(ffn));
   const dim3 grid1(unsigned(slots * g1));
@@ -331,23 +346,36 @@ hipError_t launch_gather_swiglu(const void* rows, int64_t n_rows, int64_t hidden
   const uint16_t* wu = static_cast<const uint16_t*>(w_up);
   if (hidden % 256 == 0)
     gather_gemm_kernel<0, 256, 2><<<grid1, kThreads, 0, stream>>>(
-        r16, int(hidden), order, passes, n_passes, g1, wg, wu, int(ffn), h, int(ffn));
+        r16, int(hidden), order, passes, n_passes, g1, wg, wu, int(ffn), h, int(ffn), none);
   else
     gather_gemm_kernel<0, 128, 4><<<grid1, kThreads, 0, stream>>>(
-        r16, int(hidden), order, passes, n_passes, g1, wg, wu, int(ffn), h, int(ffn));
+        r16, int(hidden), order, passes, n_passes, g1, wg, wu, int(ffn), h, int(ffn), none);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // 4. down: 256 D columns per workgroup, K = F
+  // 4. down: 256 D columns per workgroup, K = F; y stored, or the combine fused
   const int g2 = int(groups_down(hidden));
   const dim3 grid2(unsigned(slots * g2));
   const uint16_t* wd = static_cast<const uint16_t*>(w_down);
   uint16_t* y16 = static_cast<uint16_t*>(y);
-  if (ffn % 256 == 0)
+  const bool k256 = ffn % 256 == 0;
+  if (fused) {
+    if (k256)
+      gather_gemm_kernel<2, 256, 2><<<grid2, kThreads, 0, stream>>>(
+          h, int(ffn), order, passes, n_passes, g2, wd, nullptr, int(hidden), nullptr,
+          int(hidden), *fused);
+    else
+      gather_gemm_kernel<2, 128, 4><<<grid2, kThreads, 0, stream>>>(
+          h, int(ffn), order, passes, n_passes, g2, wd, nullptr, int(hidden), nullptr,
+          int(hidden), *fused);
+  } else if (k256) {
     gather_gemm_kernel<1, 256, 2><<<grid2, kThreads, 0, stream>>>(
-        h, int(ffn), order, passes, n_passes, g2, wd, nullptr, int(hidden), y16, int(hidden));
-  else
+        h, int(ffn), order, passes, n_passes, g2, wd, nullptr, int(hidden), y16, int(hidden),
+        none);
+  } else {
     gather_gemm_kernel<1, 128, 4><<<grid2, kThreads, 0, stream>>>(
-        h, int(ffn), order, passes, n_passes, g2, wd, nullptr, int(hidden), y16, int(hidden));
+        h, int(ffn), order, passes, n_passes, g2, wd, nullptr, int(hidden), y16, int(hidden),
+        none);
+  }
   return hipGetLastError();
 }
 

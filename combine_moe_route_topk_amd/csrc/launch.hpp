@@ -90,12 +90,24 @@ hipError_t launch_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidde
 // SwiGLU experts over rows in any order, row r taking expert row_expert[r]
 // (hidden and ffn multiples of 128).  tiles: workgroup count of the larger
 // of the two products, for the caller's int32 range check.
+//
+// With `fused`, y is not written: the down product adds topk_w[q] * y(r)
+// straight into out[q / k] (fp32, [N, D]), q = row_pair[r] (q = r if row_pair
+// is null); rows whose q lies outside [0, n_pairs) add nothing.
+struct FusedCombine {
+  const int32_t* row_pair;
+  const float* topk_w;
+  float* out;
+  int k;
+  int n_pairs;
+};
 size_t gather_swiglu_workspace_bytes(int64_t n_rows, int n_experts, int64_t hidden, int64_t ffn);
 int64_t gather_swiglu_tiles(int64_t n_rows, int n_experts, int64_t hidden, int64_t ffn);
 hipError_t launch_gather_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                                 const int32_t* row_expert, int n_experts, const void* w_gate,
                                 const void* w_up, const void* w_down, int64_t ffn, void* y,
-                                void* workspace, hipStream_t stream);
+                                void* workspace, hipStream_t stream,
+                                const FusedCombine* fused = nullptr);
 
 // fp8 block-scaled grouped GEMM (K and N multiples of 128).
 hipError_t launch_grouped_gemm_fp8(const void* rows, const float* row_scales, int64_t n_rows,

@@ -320,6 +320,35 @@ int moe_gather_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                       const void* w_gate, const void* w_up, const void* w_down, int64_t ffn,
                       void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_gather_swiglu_combine -- moe_gather_swiglu with the weighted top-k
+ * sum fused into its down product (the zero-copy combine planned in [MLX-EP]):
+ * y is never written.  For every row r whose expert e = row_expert[r] lies in
+ * [0, E) and whose pair q (row_pair[r], or r itself when row_pair is null)
+ * lies in [0, n_tokens * k):
+ *   out[q / k] += topk_w[q] * (W_down[e] h),  h as in moe_gather_swiglu,
+ * with the product's fp32 value (y is not rounded to bf16) added by fp32
+ * atomics.  out accumulates: pass zeros for the plain combine, or the residual
+ * stream to add the layer into it.  The order of the k additions into one
+ * element is not fixed, so results can differ between calls in the last bits
+ * of fp32 (the unfused moe_gather_swiglu + moe_combine pair is bit-stable).
+ *
+ *   rows            [n_rows, D] bfloat16, any order (e.g. the unsorted dispatch)
+ *   row_expert      [n_rows] int32;  row_pair [n_rows] int32 or null (the
+ *                   dispatch's src_pair: the pair q = t*k + j each row holds)
+ *   topk_w          [n_tokens, k] float32 (the routing weights)
+ *   out             [n_tokens, D] float32, read and written
+ *   w_gate, w_up    [E, F, D] bfloat16;  w_down [E, D, F] bfloat16
+ *   workspace       moe_gather_swiglu_workspace_bytes(n_rows, E, D, F) bytes
+ * Errors: those of moe_gather_swiglu, with k outside [1, 64] or n_tokens < 0
+ * as MOE_ERR_ARG, n_tokens * k beyond the int32 range or out / topk_w not
+ * 4-byte aligned as MOE_ERR_UNSUPPORTED. */
+int moe_gather_swiglu_combine(const void* rows, int64_t n_rows, int64_t hidden,
+                              const int32_t* row_expert, const int32_t* row_pair,
+                              const float* topk_w, int64_t n_tokens, int32_t k, int32_t n_experts,
+                              const void* w_gate, const void* w_up, const void* w_down,
+                              int64_t ffn, float* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* moe_grouped_gemm_fp8 -- fp8 block-scaled grouped expert GEMM reading the
  * dispatched fp8 rows in place ([1SIDED]: the dispatch is agnostic to the
  * activation quantisation format, and grouped GEMMs read the received buffers

@@ -227,3 +227,23 @@ def test_gather_swiglu_errors():
     assert g(FAKE, 8, 128, FAKE, 4, FAKE, FAKE, FAKE, 128, FAKE, ctypes.c_void_p(0x1080), need,
              None) == WS
     assert g(None, 0, 128, None, 4, None, None, None, 128, None, None, 0, None) == 0   # empty
+
+
+def test_gather_swiglu_combine_errors():
+    g = lib.moe_gather_swiglu_combine
+    need = lib.moe_gather_swiglu_workspace_bytes(16, 4, 128, 128)
+    args = lambda **kw: [kw.get("rows", FAKE), kw.get("n_rows", 16), kw.get("d", 128), FAKE,
+                         kw.get("row_pair", None), kw.get("tw", FAKE), kw.get("n", 8), kw.get("k", 2),
+                         kw.get("e", 4), FAKE, FAKE, FAKE, kw.get("f", 128), kw.get("out", FAKE),
+                         kw.get("ws", FAKE), kw.get("wsb", need), None]
+    assert g(*args(n_rows=-1)) == ARG
+    assert g(*args(n=-1)) == ARG
+    assert g(*args(k=0)) == ARG and g(*args(k=65)) == ARG
+    assert g(*args(e=2000)) == UNSUP
+    assert g(*args(d=192)) == UNSUP and g(*args(f=64)) == UNSUP
+    assert g(*args(n=1 << 30, k=4)) == UNSUP
+    assert g(*args(tw=None)) == ARG and g(*args(out=None)) == ARG and g(*args(rows=None)) == ARG
+    assert g(*args(out=ctypes.c_void_p(0x1002))) == UNSUP
+    assert g(*args(rows=ctypes.c_void_p(0x1008))) == UNSUP
+    assert g(*args(wsb=need - 1)) == WS and g(*args(ws=ctypes.c_void_p(0x1040))) == WS
+    assert g(*args(n_rows=0, rows=None, tw=None, out=None, ws=None, wsb=0)) == 0

@@ -8,7 +8,7 @@ import torch
 import combine_moe_route_topk_amd as moe
 from oracle import codecs
 from oracle.combine import combine_f64
-from oracle.swiglu import swiglu_rows
+from oracle.swiglu import swiglu_combine, swiglu_rows
 from tests.gpu_util import DEV, check_combine, check_swiglu, to_dev, to_np
 from workloads import DECODE_FFN, make_inputs, make_swiglu_weights_device
 
@@ -135,3 +135,96 @@ def test_gather_swiglu_multi_workgroup_grouping():
     w = _weights(rng, e, d, f)
     got = _run(rows, experts, w)
     check_swiglu(got, swiglu_rows(rows, experts, *w), experts, what="E=300 R=5000")
+
+
+# ------------------------------------------------------------------ the combine fused in
+
+def check_fused(got, ref, what=""):
+    """got float32 [N, D] from the GPU, ref float64 from oracle.swiglu.swiglu_combine:
+    the expert FFN tolerance (2e-2 of max(|o|, rms of the token's row)), the
+    k weighted terms and the residual summed in fp32 on the GPU."""
+    g = np.asarray(got, np.float64)
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    bad = np.abs(g - ref) > 2e-2 * np.maximum(np.abs(ref), rms)
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} elements outside 2e-2"
+    rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert rel <= 5e-3, f"{what}: relative error {rel:.3e}"
+
+
+@pytest.mark.parametrize("n,k,e,d,f,shuffle", [
+    (12, 4, 5, 256, 256, True),       # rows in a shuffled layout, row_pair given
+    (40, 2, 3, 384, 128, False),      # identity layout (row_pair null), K = 384 path
+    (7, 8, 16, 128, 512, True),
+    (33, 1, 2, 512, 256, False),      # k = 1
+])
+def test_gather_swiglu_combine_small(n, k, e, d, f, shuffle):
+    rng = np.random.default_rng(n * 31 + k)
+    r = n * k
+    experts = rng.integers(0, e, r).astype(np.int32)
+    rows = _bf16(rng.standard_normal((r, d)))
+    w = _weights(rng, e, d, f)
+    tw = rng.uniform(0.05, 1.0, (n, k)).astype(np.float32)
+    out0 = rng.standard_normal((n, d)).astype(np.float32)          # a residual to add into
+    row_pair = rng.permutation(r).astype(np.int32) if shuffle else np.arange(r, dtype=np.int32)
+    out = to_dev(out0.copy())
+    moe.moe_gather_swiglu_combine(to_dev(rows), to_dev(experts), to_dev(tw), *map(to_dev, w),
+                                  row_pair=to_dev(row_pair) if shuffle else None, out=out)
+    torch.cuda.synchronize()
+    ref = swiglu_combine(rows, experts, row_pair, tw, k, *w, out0=out0)
+    check_fused(to_np(out), ref, what=f"N={n} k={k} E={e} D={d} F={f}")
+
+
+def test_gather_swiglu_combine_skips_rows_without_pair_or_expert():
+    rng = np.random.default_rng(8)
+    n, k, e, d, f = 6, 2, 3, 128, 128
+    experts = rng.integers(0, e, n * k).astype(np.int32)
+    experts[3] = -1                                     # no expert
+    row_pair = np.arange(n * k, dtype=np.int32)
+    row_pair[5] = n * k + 7                             # no pair
+    rows = _bf16(rng.standard_normal((n * k, d)))
+    w = _weights(rng, e, d, f)
+    tw = rng.uniform(0.1, 1.0, (n, k)).astype(np.float32)
+    out = moe.moe_gather_swiglu_combine(to_dev(rows), to_dev(experts), to_dev(tw), *map(to_dev, w),
+                                        row_pair=to_dev(row_pair))
+    torch.cuda.synchronize()
+    keep = np.ones(n * k, bool)
+    keep[[3, 5]] = False
+    ref = swiglu_combine(rows[keep], experts[keep], row_pair[keep], tw, k, *w)
+    check_fused(to_np(out), ref, what="skipped rows")
+
+
+def test_decode_layer_fused_combine_full_size():
+    """The decode layer with the combine fused into the down product (N=128,
+    D=7168, E=256, top-8, F=2048, unsorted identity layout).  Three tokens
+    against the oracle (their 24 rows, the experts' weights copied back); all
+    tokens against the unfused path (per-row FFN in bf16, then the combine in
+    fp32), which differs only by the bf16 rounding of y: at most 2^-8 of
+    sum_j |w_j y_j| per element, plus fp32 sums."""
+    cfg = DECODE_FFN
+    inp = make_inputs(cfg)
+    w = make_swiglu_weights_device(cfg)
+    idx, tw, res = moe.moe_route_dispatch(to_dev(inp["logits"]), to_dev(inp["x"]), cfg.top_k,
+                                          cfg.n_segments, cfg.renormalize, cfg.sort, cfg.sort_cutoff)
+    fused = moe.moe_gather_swiglu_combine(res.rows, res.row_expert, tw, w["w_gate"], w["w_up"],
+                                          w["w_down"], row_pair=res.src_pair)
+    y = moe.moe_gather_swiglu(res.rows, res.row_expert, w["w_gate"], w["w_up"], w["w_down"])
+    unfused = moe.moe_combine(y, res.dst_pos, tw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    k = cfg.top_k
+    yf = codecs.bf16_bits_to_f32(to_np(y)).astype(np.float64)
+    mag = combine_f64(np.abs(yf), to_np(res.dst_pos), np.abs(to_np(tw)), k)
+    diff = np.abs(to_np(fused).astype(np.float64) - to_np(unfused).astype(np.float64))
+    assert (diff <= 2.0 ** -8 * mag + 1e-6 * mag + 1e-30).all(), float(np.max(diff - 2.0 ** -8 * mag))
+    toks = np.array([0, 57, 127])
+    rexp = to_np(res.row_expert)
+    sel_rows = np.concatenate([np.arange(t * k, (t + 1) * k) for t in toks])   # identity layout
+    chosen = np.unique(rexp[sel_rows])
+    host = {nm: v.index_select(0, torch.from_numpy(chosen).to(DEV)).view(torch.int16).cpu()
+            .numpy().view(np.uint16) for nm, v in w.items()}
+    local = np.searchsorted(chosen, rexp[sel_rows])
+    tw_np = to_np(tw)
+    # the three tokens renumbered 0..2 with their own rows, pairs and weights
+    row_pair = np.arange(toks.size * k)
+    ref = swiglu_combine(to_np(res.rows)[sel_rows], local, row_pair, tw_np[toks], k,
+                         host["w_gate"], host["w_up"], host["w_down"])
+    check_fused(to_np(fused)[toks], ref, what="decode fused combine")
