@@ -93,3 +93,55 @@ def test_grouped_gemm_fp8_replays():
     sw = to_dev(rng.uniform(0.01, 1, (e, n // 128, k // 128)).astype(np.float32))
     y = torch.empty((250, n), dtype=torch.bfloat16, device=DEV)
     _replay_matches(lambda: moe.moe_grouped_gemm_fp8(rows, sx, offs, w, sw, y=y), [y], lambda: y.zero_())
+
+
+def _gather_case(seed=5, e=6, d=256, f=256, r=90):
+    rng = np.random.default_rng(seed)
+    bits = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(DEV)
+    experts = rng.integers(0, e, r).astype(np.int32)
+    experts[:20] = 2                                     # one expert with two passes
+    rows = bits(rng.standard_normal((r, d)))
+    w = (bits(rng.standard_normal((e, f, d)) * 0.05), bits(rng.standard_normal((e, f, d)) * 0.05),
+         bits(rng.standard_normal((e, d, f)) * 0.05))
+    ws = torch.empty(moe.moe_gather_swiglu_workspace_bytes(r, e, d, f), dtype=torch.uint8, device=DEV)
+    return rng, to_dev(experts), rows, w, ws
+
+
+def test_gather_swiglu_replays():
+    """The id grouping, the pass list and both products are recomputed on every
+    replay (the workspace is clobbered too)."""
+    _, experts, rows, w, ws = _gather_case()
+    y = torch.empty_like(rows)
+    _replay_matches(lambda: moe.moe_gather_swiglu(rows, experts, *w, y=y, workspace=ws), [y],
+                    lambda: (y.zero_(), ws.zero_()))
+
+
+def test_gather_swiglu_combine_replays():
+    """The fused combine adds into out with fp32 atomics in no fixed order, so
+    replays are compared with the eager call to fp32 rounding, not bit for bit."""
+    rng, experts, rows, w, ws = _gather_case(seed=6, r=96)
+    k = 4
+    tw = to_dev(rng.uniform(0.1, 1.0, (96 // k, k)).astype(np.float32))
+    pairs = to_dev(rng.permutation(96).astype(np.int32))
+    out = torch.empty((96 // k, rows.shape[1]), dtype=torch.float32, device=DEV)
+
+    def step():
+        out.zero_()
+        moe.moe_gather_swiglu_combine(rows, experts, tw, *w, row_pair=pairs, out=out, workspace=ws)
+
+    step()
+    _sync()
+    eager = to_np(out).astype(np.float64)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        out.fill_(7.0)
+        ws.zero_()
+        _sync()
+        g.replay()
+        _sync()
+        got = to_np(out).astype(np.float64)
+        # terms are O(0.1); a different order of the k fp32 additions moves a sum
+        # by a few fp32 ulps of them, a missing term by O(0.1)
+        assert np.all(np.abs(got - eager) <= 1e-6 * (np.abs(eager) + 1.0)), rep
