@@ -228,3 +228,17 @@ def test_decode_layer_fused_combine_full_size():
     ref = swiglu_combine(to_np(res.rows)[sel_rows], local, row_pair, tw_np[toks], k,
                          host["w_gate"], host["w_up"], host["w_down"])
     check_fused(to_np(fused)[toks], ref, what="decode fused combine")
+
+
+def test_gather_swiglu_max_experts():
+    """E = 1024 (the library's maximum): one plan thread per expert, many empty
+    experts, a few with several passes."""
+    rng = np.random.default_rng(9)
+    e, d, f = 1024, 128, 128
+    experts = rng.integers(0, e, 2000).astype(np.int32)
+    experts[:50] = 1023                                  # the last expert, four passes
+    experts[50:70] = 0
+    rows = _bf16(rng.standard_normal((experts.size, d)))
+    w = _weights(rng, e, d, f)
+    got = _run(rows, experts, w)
+    check_swiglu(got, swiglu_rows(rows, experts, *w), experts, what="E=1024")
