@@ -443,7 +443,7 @@ def _blas_threads():
         return 1
 
 
-def _time_oracle(fn, min_seconds=10.0, max_repeats=5):
+def _time_oracle(fn, min_seconds=10.0, max_repeats=200):
     times = []
     while len(times) < max_repeats and (len(times) < 1 or sum(times) < min_seconds):
         t0 = time.perf_counter()
@@ -512,7 +512,7 @@ def cpu_oracle_gather_swiglu(torch, res, w, n_experts_sample=2):
                        f"of {n} passes ({tot:.1f} s)", seconds_per_pass=round(dt, 3))
 
 
-def cpu_baseline(cfg, n_sample, min_seconds=10.0, max_repeats=5):
+def cpu_baseline(cfg, n_sample, min_seconds=10.0, max_repeats=20):
     """The oracle as it stands, on the first ``n_sample`` tokens of the same
     workload, repeated until ~min_seconds of CPU work; median pass time."""
     from oracle import codecs, dispatch as od
