@@ -125,3 +125,38 @@ def test_fused_combine_invariant_under_row_shuffle_and_skips_bad_ids():
     t0 = row_pair[0] // k
     others = np.arange(tw.shape[0]) != t0
     assert np.array_equal(c[others], a[others]) and not np.allclose(c[t0], a[t0])
+
+
+from hypothesis import given, settings, strategies as st
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(1, 4), st.integers(1, 3), st.integers(1, 3), st.integers(1, 5), st.integers(1, 5),
+       st.integers(0, 2**32 - 1))
+def test_fused_combine_brute_force_sweep(n, k, e, d, f, seed):
+    """Random small shapes, rows in a shuffled layout, some rows with an expert
+    outside [0, E): the fused combine against a pure-Python evaluation that
+    looks each pair's row up by scanning the rows."""
+    rng = np.random.default_rng(seed)
+    wg, wu = _bf16(rng.standard_normal((e, f, d)) * 0.5), _bf16(rng.standard_normal((e, f, d)) * 0.5)
+    wd = _bf16(rng.standard_normal((e, d, f)) * 0.5)
+    rows = _bf16(rng.standard_normal((n * k, d)))
+    experts = rng.integers(-1, e + 1, n * k)               # -1 and e take no part
+    row_pair = rng.permutation(n * k)
+    tw = rng.uniform(0.05, 1.0, (n, k)).astype(np.float32)
+    got = swiglu_combine(rows, experts, row_pair, tw, k, wg, wu, wd)
+    dec = lambda b: codecs.bf16_bits_to_f32(b).astype(np.float64).tolist()
+    for t in range(n):
+        terms = [[] for _ in range(d)]
+        for j in range(k):
+            r = [rr for rr in range(n * k) if row_pair[rr] == t * k + j][0]
+            ex = experts[r]
+            if not 0 <= ex < e:
+                continue
+            y = swiglu_brute(dec(rows[r]), dec(wg[ex]), dec(wu[ex]), dec(wd[ex]))
+            for i in range(d):
+                terms[i].append(float(tw[t, j]) * y[i])
+        for i in range(d):
+            ref = math.fsum(terms[i])
+            mag = math.fsum(abs(v) for v in terms[i])
+            assert abs(got[t, i] - ref) <= 1e-3 * mag + 1e-12, (t, i)
