@@ -284,6 +284,8 @@ def moe_grouped_swiglu(rows: torch.Tensor, expert_offsets: torch.Tensor, w_gate:
     if y is None:
         y = torch.empty_like(rows)
     _need(y, "y", (torch.bfloat16,), dev)
+    if tuple(y.shape) != (r, d):
+        raise ValueError("moe_grouped_swiglu: y must be [R, D]")
     if workspace is None:
         workspace = torch.empty(max(moe_grouped_swiglu_workspace_bytes(r, e, d, f), 256),
                                 dtype=torch.uint8, device=dev)
@@ -317,6 +319,8 @@ def moe_gather_swiglu(rows: torch.Tensor, row_expert: torch.Tensor, w_gate: torc
     if y is None:
         y = torch.empty_like(rows)
     _need(y, "y", (torch.bfloat16,), dev)
+    if tuple(y.shape) != (r, d):
+        raise ValueError("moe_gather_swiglu: y must be [R, D]")
     if workspace is None:
         workspace = torch.empty(max(moe_gather_swiglu_workspace_bytes(r, e, d, f), 256),
                                 dtype=torch.uint8, device=dev)
