@@ -19,7 +19,9 @@ from ._lib import (MOE_BF16, MOE_F32, MOE_F8E4M3, MOE_SORT_AUTO, MoeError, check
 __all__ = ["moe_route_topk", "moe_resolve_sorted", "moe_dispatch_workspace_bytes", "moe_dispatch",
            "moe_combine", "moe_dequant_rows", "moe_scatter_rows", "moe_gather_rows",
            "moe_route_dispatch", "moe_route_dispatch_workspace_bytes", "moe_grouped_swiglu_workspace_bytes",
-           "moe_grouped_swiglu", "moe_abi_version", "DispatchResult", "MoeError"]
+           "moe_grouped_swiglu", "moe_grouped_gemm_fp8", "moe_gather_swiglu_workspace_bytes",
+           "moe_gather_swiglu", "moe_gather_swiglu_combine", "moe_abi_version", "DispatchResult",
+           "MoeError"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
