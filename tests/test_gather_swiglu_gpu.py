@@ -242,3 +242,27 @@ def test_gather_swiglu_max_experts():
     w = _weights(rng, e, d, f)
     got = _run(rows, experts, w)
     check_swiglu(got, swiglu_rows(rows, experts, *w), experts, what="E=1024")
+
+
+def test_gather_swiglu_random_shapes():
+    """A seeded sweep of 12 shapes: D and F over multiples of 128 (both chunk
+    widths), expert counts from 1 to 40, row counts from 1 to 700 with
+    Zipf-like skew, some ids out of range."""
+    master = np.random.default_rng(11)
+    for case in range(12):
+        e = int(master.integers(1, 41))
+        d = 128 * int(master.integers(1, 7))
+        f = 128 * int(master.integers(1, 5))
+        r = int(master.integers(1, 701))
+        p = 1.0 / np.arange(1, e + 1) ** 1.1
+        experts = master.choice(e, r, p=p / p.sum()).astype(np.int32)
+        experts[master.random(r) < 0.03] = -1
+        rows = _bf16(master.standard_normal((r, d)))
+        w = _weights(master, e, d, f)
+        y0 = torch.full((r, d), 3.0, dtype=torch.bfloat16, device=DEV)
+        got = _run(rows, experts, w, y=y0)
+        ok = experts >= 0
+        assert (codecs.bf16_bits_to_f32(got[~ok]) == 3.0).all(), case
+        if ok.any():
+            check_swiglu(got[ok], swiglu_rows(rows[ok], experts[ok], *w), experts[ok],
+                         what=f"case {case}: E={e} D={d} F={f} R={r}")
