@@ -10,11 +10,12 @@ Zipf(1.1) expert popularity, sorted dispatch.  The decode shape (N=128,
 unsorted dispatch) is timed in the same run and reported as µs/layer beside
 it.
 
-Timing: K steps are timed as K replays of the step captured once in a HIP
-graph (the launch sequence a serving loop would replay), bracketed by
-synchronizations on the wall clock; K eager steps with HIP events recorded on
-the launch stream give the per-stage times and the dominant kernel's
-duration.
+Timing: the K timed steps are captured as one HIP graph of K consecutive
+layers (the launch sequence a serving loop replays for a whole forward pass)
+and replayed once, bracketed by synchronizations on the wall clock; K replays
+of a one-step graph give the figure with a graph launch per layer; K eager
+steps with HIP events recorded on the launch stream give the per-stage times
+and the dominant kernel's duration.
 
 Output: one JSON line with the whole-path GB/s of algorithmic bytes, a
 roofline object for the dominant kernel and the CPU oracle timed on a bounded
@@ -143,30 +144,42 @@ def time_path(path, steps, warmup):
     return wall / steps * 1e3, stage.mean(axis=0) * 1e3, np.median(stage, axis=0) * 1e3
 
 
-def capture(path):
-    """The step captured once in a HIP graph (torch.cuda.CUDAGraph)."""
-    torch = path.torch
-    path.step()
+def capture(torch, step, n):
+    """n consecutive calls of step() captured in one HIP graph (torch.cuda.CUDAGraph)."""
+    step()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        path.step()
+        for _ in range(n):
+            step()
     return g
 
 
-def time_graph(path, steps, warmup):
-    """K replays of the captured step between two synchronizations, on the
-    wall clock: removes host launch overhead, which dominates at decode size."""
-    torch = path.torch
-    g = capture(path)
+def graph_times(torch, step, steps, warmup):
+    """Per-step wall time of the step in HIP graphs, in ms.
+
+    Timed steps: K consecutive steps captured as one graph, the way a serving
+    loop captures a whole forward pass of K layers, replayed once between two
+    synchronizations.  Untimed before it: W replays of a one-step graph, then
+    one replay of the K-step graph (its one-time upload to the device).  The
+    one-step graph is also timed over K replays: that figure includes the
+    launch of a graph per step.  Returns (K-step graph, one-step graph)."""
+    g1 = capture(torch, step, 1)
     for _ in range(warmup):
-        g.replay()
+        g1.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        g.replay()
+        g1.replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e3
+    one = (time.perf_counter() - t0) / steps * 1e3
+    gk = capture(torch, step, steps)
+    gk.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gk.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3, one
 
 
 def check_outputs(path):
@@ -210,7 +223,8 @@ def dc_bytes(cfg):
 
 def time_all_configs(torch, moe, steps, warmup):
     """route -> dispatch (maps and rows) -> combine for each of the five
-    workloads, captured in a HIP graph and replayed.  Expert outputs are an
+    workloads, timed as in graph_times (K consecutive steps in one graph; the
+    one-step graph's figure beside it).  Expert outputs are an
     input of the combine: identity experts read the dispatched rows; the fp8
     workload's identity expert (dequantisation to bf16) runs once before the
     timing.  The segment-major workload alternates the sort flag per call, so
@@ -242,22 +256,13 @@ def time_all_configs(torch, moe, steps, warmup):
                                        x_scales=xs, topk_idx=idx, topk_w=w, workspace=ws, out=res)
                 moe.moe_combine(y, res.dst_pos, w, out=o)
 
-        step()
-        torch.cuda.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            step()
-        for _ in range(warmup):
-            gr.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         reps = max(steps, 50)
-        for _ in range(reps):
-            gr.replay()
-        torch.cuda.synchronize()
-        us = (time.perf_counter() - t0) / reps / len(sorts) * 1e6
+        ms_k, ms_1 = graph_times(torch, step, reps, warmup)
+        us = ms_k * 1e3 / len(sorts)
+        us1 = ms_1 * 1e3 / len(sorts)
         b = dc_bytes(cfg)["total"]
-        out[name] = {"us_per_layer": round(us, 2), "GB_per_s": round(b / (us * 1e-6) / 1e9, 1),
+        out[name] = {"us_per_layer": round(us, 2), "us_per_layer_graph1": round(us1, 2),
+                     "GB_per_s": round(b / (us * 1e-6) / 1e9, 1),
                      "frac_of_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "bytes": b, "mode": "alternating unsorted/sorted" if len(sorts) > 1 else
                      ("sorted" if res.sorted else "unsorted")}
@@ -576,7 +581,7 @@ def main():
     path = Path(cfg, torch, moe)
     ms_eager, stage_mean_us, stage_med_us = time_path(path, args.steps, args.warmup)
     check_outputs(path)
-    ms = time_graph(path, args.steps, args.warmup)       # the timed steps
+    ms, ms_g1 = graph_times(torch, path.step, args.steps, args.warmup)   # the timed steps
     check_outputs(path)
     n, d, e, k, g = cfg.n_tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.n_segments
     b = algorithmic_bytes(n, d, e, k, g, cfg.elem_bytes)
@@ -614,9 +619,11 @@ def main():
                    "n_experts": e, "top_k": k, "n_segments": g,
                    "sort": "sorted" if path.res.sorted else "unsorted", "experts": "identity",
                    "bytes_per_step": b["total"]},
-        "timing": "K replays of the step captured in a HIP graph, wall clock between "
-                  "synchronizations; stages from HIP events over K eager steps",
+        "timing": "K consecutive steps captured as one HIP graph (a K-layer forward pass), "
+                  "replayed once, wall clock between synchronizations; graph1 = K replays "
+                  "of a one-step graph; stages from HIP events over K eager steps",
         "us_per_layer": round(ms * 1e3, 2),
+        "us_per_layer_graph1": round(ms_g1 * 1e3, 2),
         "us_per_layer_eager": round(ms_eager * 1e3, 2),
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "stages_us": {nm: round(float(v), 2) for nm, v in zip(names, stage_mean_us)},
@@ -629,9 +636,10 @@ def main():
         check_outputs(dpath)
         db = algorithmic_bytes(dcfg.n_tokens, dcfg.hidden, dcfg.n_experts, dcfg.top_k,
                                dcfg.n_segments, dcfg.elem_bytes)
-        gms = time_graph(dpath, max(args.steps, 200), args.warmup)
+        gms, gms1 = graph_times(torch, dpath.step, max(args.steps, 200), args.warmup)
         check_outputs(dpath)
         rec["decode"] = {"workload": f"decode: {dcfg.note}", "us_per_layer": round(gms * 1e3, 2),
+                         "us_per_layer_graph1": round(gms1 * 1e3, 2),
                          "us_per_layer_eager": round(dms * 1e3, 2),
                          "calls": "moe_route_dispatch (with rows) + moe_combine",
                          "GB_per_s": round(db["total"] / (gms * 1e-3) / 1e9, 1),
