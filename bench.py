@@ -561,6 +561,26 @@ def calib_copy(torch):
     print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
 
 
+def copy_ceiling(torch, nbytes, reps=10):
+    """A plain device copy moving the same bytes as one step (half read, half
+    written), timed with HIP events: the copy ceiling the path is compared with."""
+    half = nbytes // 2 // 16 * 16
+    a = torch.empty(half, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return {"GB_per_s": round(2 * half / (ms * 1e-3) / 1e9, 1), "bytes_moved": 2 * half,
+            "what": "torch device-to-device copy of half the step's bytes (read + write)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -586,6 +606,7 @@ def main():
     n, d, e, k, g = cfg.n_tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.n_segments
     b = algorithmic_bytes(n, d, e, k, g, cfg.elem_bytes)
     value = b["total"] / (ms * 1e-3) / 1e9
+    ceiling = copy_ceiling(torch, b["total"])
 
     names = ["route+maps", "scatter", "combine"]
     dom = "scatter" if stage_mean_us[1] >= stage_mean_us[2] else "combine"
@@ -626,6 +647,8 @@ def main():
         "us_per_layer_graph1": round(ms_g1 * 1e3, 2),
         "us_per_layer_eager": round(ms_eager * 1e3, 2),
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "copy_ceiling": ceiling,
+        "frac_of_copy_ceiling": round(value / ceiling["GB_per_s"], 4),
         "stages_us": {nm: round(float(v), 2) for nm, v in zip(names, stage_mean_us)},
         "roofline": roofline,
     }
