@@ -82,6 +82,8 @@ hipError_t launch_dequant_rows(const uint8_t* rows, const float* row_scales, int
                                int64_t hidden, uint16_t* y, hipStream_t stream);
 
 size_t grouped_swiglu_workspace_bytes(int64_t n_rows, int n_experts, int64_t hidden, int64_t ffn);
+// Worst-case workgroup count of the larger of the two grouped SwiGLU launches.
+int64_t grouped_swiglu_tiles(int64_t n_rows, int n_experts, int64_t hidden, int64_t ffn);
 hipError_t launch_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                                  const int32_t* expert_offsets, int n_experts, const void* w_gate,
                                  const void* w_up, const void* w_down, int64_t ffn, void* y,

@@ -280,8 +280,9 @@ size_t moe_grouped_swiglu_workspace_bytes(int64_t n_rows, int32_t n_experts, int
  *   w_gate, w_up    [E, F, D] bfloat16;  w_down [E, D, F] bfloat16
  *   y               [n_rows, D] bfloat16, output, same row order as rows
  * Errors: MOE_ERR_ARG for null pointers (unless n_rows == 0), sizes < 1;
- * MOE_ERR_UNSUPPORTED for D % 64 != 0, F % 64 != 0, E > MOE_MAX_EXPERTS, or
- * rows, a weight tensor or y not 16-byte aligned;
+ * MOE_ERR_UNSUPPORTED for D % 64 != 0, F % 64 != 0, D or F above 2^22,
+ * E > MOE_MAX_EXPERTS, more than 2^31 tiles of 256 x 256, or rows, a weight
+ * tensor or y not 16-byte aligned;
  * MOE_ERR_WORKSPACE for a short workspace or one not 256-byte aligned. */
 int moe_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                        const int32_t* expert_offsets, int32_t n_experts,

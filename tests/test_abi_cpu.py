@@ -142,6 +142,13 @@ def test_dequant_and_swiglu_errors():
     assert g(FAKE, 16, 64, FAKE, 8, FAKE, FAKE, odd, 128, FAKE, FAKE, 1 << 30, None) == UNSUP
     assert g(FAKE, 16, 64, FAKE, 8, FAKE, FAKE, FAKE, 128, odd, FAKE, 1 << 30, None) == UNSUP
     assert b"16-byte" in lib.moe_last_error()
+    # K above 2^22 (32-bit per-lane load offsets within a 256-row tile)
+    assert g(FAKE, 16, (1 << 22) + 64, FAKE, 8, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1 << 62, None) == UNSUP
+    assert g(FAKE, 16, 64, FAKE, 8, FAKE, FAKE, FAKE, (1 << 22) + 64, FAKE, FAKE, 1 << 62, None) == UNSUP
+    assert b"at most" in lib.moe_last_error()
+    # more tiles than a launch can index
+    assert g(FAKE, (1 << 31) - 1, 64, FAKE, 8, FAKE, FAKE, FAKE, 1 << 22, FAKE, FAKE, 1 << 62, None) == UNSUP
+    assert b"too many tiles" in lib.moe_last_error()
 
 
 def test_row_copy_errors():
