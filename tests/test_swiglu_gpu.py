@@ -81,3 +81,52 @@ def test_mixtral_layer_full_size():
     exact = combine_f64(yf, to_np(res.dst_pos), to_np(tw), cfg.top_k, tokens=toks)
     mag = combine_f64(np.abs(yf), to_np(res.dst_pos), np.abs(to_np(tw)), cfg.top_k, tokens=toks)
     check_combine(to_np(out)[toks], exact, mag, True, what="mixtral combine")
+
+
+def test_grouped_swiglu_many_experts():
+    """E = 300: the device's tile count scans the offsets 64 experts at a time; many
+    experts are empty and a few span several 256-row tiles."""
+    rng = np.random.default_rng(300)
+    e, d, f = 300, 128, 192
+    sizes = rng.choice([0, 0, 0, 1, 3, 17, 255, 256, 257, 600], size=e)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    n_rows = int(offs[-1])
+    rows = _bf16(rng.standard_normal((n_rows, d)))
+    wg = _bf16(rng.standard_normal((e, f, d)) * 0.05)
+    wu = _bf16(rng.standard_normal((e, f, d)) * 0.05)
+    wd = _bf16(rng.standard_normal((e, d, f)) * 0.05)
+    y = moe.moe_grouped_swiglu(to_dev(rows), to_dev(offs), to_dev(wg), to_dev(wu), to_dev(wd))
+    torch.cuda.synchronize()
+    experts = np.repeat(np.arange(e), sizes)
+    ref = swiglu_rows(rows, experts, wg, wu, wd)
+    check_swiglu(to_np(y), ref, experts, what="E=300")
+
+
+@pytest.mark.parametrize("offs", [[0, 100, 50, 200, 180, 260], [20, 100, 50, 200, 180, 260],
+                                  [-5, 70, 400, 30, 500, 10]])
+def test_grouped_swiglu_offsets_outside_the_contract(offs):
+    """Offsets that start above 0, decrease or run past the rows are clamped into
+    [0, R] and made non-decreasing (lo_0 = clamp(offs[0]), hi_e = clamp(offs[e+1],
+    lo_e, R)): rows inside those ranges get their expert's FFN, the rest of y is
+    untouched."""
+    rng = np.random.default_rng(len(offs) + offs[0] + 7)
+    e, d, f, n_rows = len(offs) - 1, 64, 128, 300
+    rows = _bf16(rng.standard_normal((n_rows, d)))
+    wg = _bf16(rng.standard_normal((e, f, d)) * 0.05)
+    wu = _bf16(rng.standard_normal((e, f, d)) * 0.05)
+    wd = _bf16(rng.standard_normal((e, d, f)) * 0.05)
+    y = torch.full((n_rows, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    moe.moe_grouped_swiglu(to_dev(rows), to_dev(np.array(offs, np.int32)), to_dev(wg), to_dev(wu),
+                           to_dev(wd), y=y)
+    torch.cuda.synchronize()
+    experts = np.full(n_rows, -1)
+    lo = min(max(offs[0], 0), n_rows)
+    for j in range(e):
+        hi = min(max(offs[j + 1], lo), n_rows)
+        experts[lo:hi] = j
+        lo = hi
+    yy = codecs.bf16_bits_to_f32(to_np(y))
+    inside = experts >= 0
+    assert (yy[~inside] == 7.0).all()
+    ref = swiglu_rows(rows[inside], experts[inside], wg, wu, wd)
+    check_swiglu(to_np(y)[inside], ref, experts[inside], what=f"offsets {offs}")
