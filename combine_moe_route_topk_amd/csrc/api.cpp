@@ -332,7 +332,8 @@ int moe_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
   // per-lane load offsets within a 256-row tile are 32-bit
   if (hidden > (int64_t(1) << 22) || ffn > (int64_t(1) << 22))
     return fail(MOE_ERR_UNSUPPORTED, "%s: hidden and ffn must be at most %d", fn, 1 << 22);
-  if (moe::grouped_swiglu_tiles(n_rows, n_experts, hidden, ffn) > INT32_MAX - 8)
+  // the grid also holds up to 256 extra workgroups for the split parts of the last round
+  if (moe::grouped_swiglu_tiles(n_rows, n_experts, hidden, ffn) > INT32_MAX - 8 - 256)
     return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", fn);
   if (n_rows == 0) return ok();
   if (!rows || !expert_offsets || !w_gate || !w_up || !w_down || !y)

@@ -42,7 +42,15 @@
 // (workgroup b runs on XCD b % 8) owns a contiguous range of t, and within it
 // 8 row tiles x all column tiles, row tiles fastest, so the 32 workgroups an
 // XCD runs together share 8 row tiles and 4 weight tiles through its L2.
-// Workgroups past the last real tile exit.
+// Workgroups past the last unit exit.
+//
+// The last round: tiles that do not fill a whole round of workgroups (one per
+// CU) are split into K parts (an even number of stages each, at most 8 parts)
+// so that round keeps every CU busy.  Each part stores its fp32 partial tile in
+// the workspace and counts itself on the tile's counter (zeroed by a small
+// kernel at the start of every call); the part that arrives last sums the
+// partials in part order, so the result does not depend on which part that
+// was, and writes the tile.  Nothing waits on another workgroup.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -65,6 +73,9 @@ constexpr int kTI = 4;         // 32-row MFMA tiles per wave (128 rows)
 constexpr int kTJ = 4;         // 32-column MFMA tiles per wave (128 B rows)
 constexpr int kGroupM = 8;     // row tiles per group of the tile order
 constexpr int kXcds = 8;
+constexpr int kCuMax = 256;    // workgroups of the last round at most (one per CU)
+constexpr int kMaxSplit = 8;   // K parts of a last-round tile at most
+constexpr int kTileElems = kBM * kBN;   // fp32 partial of one tile
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8).
@@ -141,24 +152,65 @@ __device__ int count_row_tiles(const int32_t* __restrict__ offs, int n_experts, 
   return __builtin_amdgcn_readfirstlane(total);
 }
 
-// Workgroup b -> tile of the grouped, XCD-contiguous order (see the header).
-__device__ TileInfo find_tile(int b, int n_col_tiles, const int32_t* __restrict__ offs,
-                              int n_experts, int64_t n_rows) {
-  const int m_real = count_row_tiles(offs, n_experts, n_rows);
-  TileInfo ti{};
-  ti.valid = false;
-  const int tiles = m_real * n_col_tiles;
-  const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  const int j = b / kXcds;
-  const int t = (b % kXcds) * per_xcd + j;
-  if (j >= per_xcd || t >= tiles) return ti;
+// Tile t of the grouped order (t < tiles): 8 row tiles x all column tiles,
+// row tiles fastest.
+__device__ TileInfo grouped_tile(int t, int m_real, int n_col_tiles,
+                                 const int32_t* __restrict__ offs, int n_experts, int64_t n_rows) {
   const int g = t / (kGroupM * n_col_tiles);
   const int m0 = g * kGroupM;
   const int gm = m_real - m0 < kGroupM ? m_real - m0 : kGroupM;
   const int i = t - g * kGroupM * n_col_tiles;
-  ti = find_row_tile(m0 + i % gm, offs, n_experts, n_rows);
+  TileInfo ti = find_row_tile(m0 + i % gm, offs, n_experts, n_rows);
   ti.n_tile = i / gm;
   return ti;
+}
+
+// The work of one launch: `full` tiles fill whole rounds of n_cus workgroups;
+// the `tail` tiles of the last, partial round are each split into `split` K
+// parts so that round keeps every CU busy.  Part results are fp32 partial
+// tiles in the workspace; the last part of a tile to finish (an atomic
+// counter per tile) sums them in part order and writes the tile.
+struct Unit {
+  TileInfo ti;
+  int part, n_parts;    // K part of the tile and the tile's number of parts
+  int tail;             // index of the tile among the split ones (n_parts > 1)
+  int unit;             // index of the part among all split parts
+};
+
+// Workgroup b (on XCD b % 8) -> unit.  Full tiles come first in dispatch
+// order: XCD x takes a contiguous range of them; then the parts of the split
+// tiles, round-robin over the XCDs.
+__device__ Unit find_unit(int b, int n_col_tiles, int kt_n, int n_cus,
+                          const int32_t* __restrict__ offs, int n_experts, int64_t n_rows) {
+  Unit u{};
+  u.ti.valid = false;
+  const int m_real = count_row_tiles(offs, n_experts, n_rows);
+  const int tiles = m_real * n_col_tiles;
+  const int full = tiles / n_cus * n_cus;      // n_cus is a multiple of kXcds
+  const int tail = tiles - full;
+  int split = 1;
+  if (tail > 0 && kt_n % 2 == 0) {
+    split = n_cus / tail;
+    split = split < kMaxSplit ? split : kMaxSplit;
+    split = split < kt_n / 2 ? split : kt_n / 2;
+    split = split > 1 ? split : 1;
+  }
+  const int j = b / kXcds, x = b % kXcds;
+  const int full_per_xcd = full / kXcds;
+  if (j < full_per_xcd) {
+    u.ti = grouped_tile(x * full_per_xcd + j, m_real, n_col_tiles, offs, n_experts, n_rows);
+    u.part = 0;
+    u.n_parts = 1;
+    return u;
+  }
+  const int v = (j - full_per_xcd) * kXcds + x;
+  if (v >= tail * split) return u;
+  u.tail = v / split;
+  u.part = v % split;
+  u.n_parts = split;
+  u.unit = v;
+  u.ti = grouped_tile(full + u.tail, m_real, n_col_tiles, offs, n_experts, n_rows);
+  return u;
 }
 
 // Global sources of this lane's direct loads.  Run r = i*4 + w of an operand
@@ -280,21 +332,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void grouped_gemm_kernel(const uint16_t* __restrict__ A, int64_t n_rows, int K,
                          const int32_t* __restrict__ offs, int n_experts,
                          const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int NB,
-                         uint16_t* __restrict__ C, int ldc, int n_col_tiles) {
+                         uint16_t* __restrict__ C, int ldc, int n_col_tiles, int n_cus,
+                         float* __restrict__ partials, int* __restrict__ counters) {
   // two distinct arrays, so the compiler can tell the slot being loaded from
   // the slot being read and adds no wait between them
   __shared__ __align__(1024) unsigned char slot0[kSlotBytes];
   __shared__ __align__(1024) unsigned char slot1[kSlotBytes];
 
-  const TileInfo ti = find_tile(blockIdx.x, n_col_tiles, offs, n_experts, n_rows);
-  if (!ti.valid) return;
+  const Unit u = find_unit(blockIdx.x, n_col_tiles, K / kBK, n_cus, offs, n_experts, n_rows);
+  if (!u.ti.valid) return;
+  const TileInfo& ti = u.ti;
+  // this part's K stages [k_lo, k_hi) (all of K unless the tile is split; parts
+  // cover an even number of stages each, so the stage sequence stays the even one)
+  int k_lo = 0, kt_n = K / kBK;
+  if (u.n_parts > 1) {
+    const int half = kt_n / 2;
+    k_lo = 2 * (u.part * half / u.n_parts);
+    kt_n = 2 * ((u.part + 1) * half / u.n_parts) - k_lo;
+  }
+  const int64_t k_byte = int64_t(k_lo) * kBK * 2;
 
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
   const int wm = w >> 1, wn = w & 1;
 
   Src src;
-  src.a_base = reinterpret_cast<const unsigned char*>(A + ti.row0 * K);
+  src.a_base = reinterpret_cast<const unsigned char*>(A + ti.row0 * K) + k_byte;
   const int q = lane >> 3, pos = lane & 7;
 #pragma unroll
   for (int i = 0; i < kLd; ++i) {
@@ -310,13 +373,13 @@ void grouped_gemm_kernel(const uint16_t* __restrict__ A, int64_t n_rows, int K,
       int64_t f = c0 + (row & (kBN / 2 - 1));
       if (f >= NB) f = NB - 1;                              // partial last column tile
       src.b_base[i] = reinterpret_cast<const unsigned char*>(
-          (row < kBN / 2 ? B0 : B1) + (int64_t(ti.expert) * NB + c0) * K);
+          (row < kBN / 2 ? B0 : B1) + (int64_t(ti.expert) * NB + c0) * K) + k_byte;
       src.b_off[i] = (int(f - c0) * K + chunk * 8) * 2;
     } else {
       const int64_t c0 = int64_t(ti.n_tile) * kBN;
       int64_t n = c0 + row;
       if (n >= NB) n = NB - 1;                              // partial last column tile
-      src.b_base[i] = reinterpret_cast<const unsigned char*>(B0 + (int64_t(ti.expert) * NB + c0) * K);
+      src.b_base[i] = reinterpret_cast<const unsigned char*>(B0 + (int64_t(ti.expert) * NB + c0) * K) + k_byte;
       src.b_off[i] = (int(n - c0) * K + chunk * 8) * 2;
     }
   }
@@ -344,7 +407,7 @@ void grouped_gemm_kernel(const uint16_t* __restrict__ A, int64_t n_rows, int K,
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   // stage d lives in slot d % 2; every wave runs the same barrier sequence
-  const int kt_n = K / kBK;                // >= 1 (K % 64 == 0), parity as TAIL says
+  // kt_n >= 1 stages from k_lo; its parity is the one TAIL says
   Frag f0, f1;
   load_runs<0, 2 * kLd>(slot0, src, 0);
   stage_barrier();                          // stage 0 landed
@@ -369,6 +432,41 @@ void grouped_gemm_kernel(const uint16_t* __restrict__ A, int64_t n_rows, int K,
     }
   }
   __builtin_amdgcn_s_waitcnt(wait_vm(0));  // no direct load may outlive the workgroup
+
+  if (u.n_parts > 1) {
+    // a part of a split tile: store the fp32 partial (element e of the lane's
+    // 256 at e * kThreads + tid, coalesced), then count the part; the last
+    // part to arrive sums all of them in part order and writes the tile
+    const int tid = threadIdx.x;
+    float* mine = partials + int64_t(u.unit) * kTileElems;
+#pragma unroll
+    for (int i = 0; i < kTI; ++i)
+#pragma unroll
+      for (int j = 0; j < kTJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mine[((i * kTJ + j) * 16 + v) * kThreads + tid] = acc[i][j][v];
+    __shared__ int s_last;
+    __threadfence();                        // the partial is visible device-wide ...
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&counters[u.tail], 1) == u.n_parts - 1;   // ... before the count
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();                        // every part's partial is visible here
+    // sum in part order, one part at a time so each part's 256 loads per lane
+    // are independent and go out together
+    for (int p = 0; p < u.n_parts; ++p) {
+      const float* part = partials + (int64_t(u.tail) * u.n_parts + p) * kTileElems + tid;
+#pragma unroll
+      for (int i = 0; i < kTI; ++i)
+#pragma unroll
+        for (int j = 0; j < kTJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float x = part[((i * kTJ + j) * 16 + v) * kThreads];
+            acc[i][j][v] = p == 0 ? x : acc[i][j][v] + x;
+          }
+    }
+  }
 
   // epilogue: lane holds C[8*(v/4) + 4*(lane/32) + v%4][lane%32] of each 32x32 tile
   const int khalf = lane >> 5;
@@ -405,42 +503,84 @@ int64_t grouped_swiglu_tiles(int64_t n_rows, int n_experts, int64_t hidden, int6
   return m * (c1 > c2 ? c1 : c2);
 }
 
+namespace {
+
+// Workspace: h [R, F] bf16 | per-launch counters of the split tiles (2 x
+// kCuMax int32) | fp32 partial tiles of the split parts (kCuMax at most).
+struct SwigluLayout {
+  size_t counters, partials, total;
+};
+
+SwigluLayout swiglu_layout(int64_t n_rows, int64_t ffn) {
+  SwigluLayout L;
+  L.counters = (size_t(n_rows) * size_t(ffn) * 2 + 255) / 256 * 256;
+  L.partials = L.counters + 2 * kCuMax * sizeof(int32_t);
+  L.total = L.partials + size_t(kCuMax) * kTileElems * sizeof(float);
+  return L;
+}
+
+__global__ void zero_counters_kernel(int32_t* __restrict__ c, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) c[i] = 0;
+}
+
+// CUs of the current device, as a multiple of kXcds in [kXcds, kCuMax].
+int cu_count() {
+  int dev = 0, n = kCuMax;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n = kCuMax;
+  n = n / kXcds * kXcds;
+  return n < kXcds ? kXcds : (n > kCuMax ? kCuMax : n);
+}
+
+}  // namespace
+
 size_t grouped_swiglu_workspace_bytes(int64_t n_rows, int n_experts, int64_t hidden, int64_t ffn) {
   (void)n_experts;
   (void)hidden;
-  return size_t(n_rows) * size_t(ffn) * 2 + 256;
+  return swiglu_layout(n_rows, ffn).total + 256;
 }
 
 hipError_t launch_grouped_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                                  const int32_t* expert_offsets, int n_experts, const void* w_gate,
                                  const void* w_up, const void* w_down, int64_t ffn, void* y,
                                  void* workspace, hipStream_t stream) {
-  // worst case of real row tiles: ceil(R / 256) plus one partial tile per expert
+  const SwigluLayout L = swiglu_layout(n_rows, ffn);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + L.counters);
+  float* partials = reinterpret_cast<float*>(ws + L.partials);
+  const int n_cus = cu_count();
+  // worst case of real row tiles: ceil(R / 256) plus one partial tile per expert;
+  // the grid also holds the extra parts of the split tiles (fewer than n_cus)
   const int max_m_tiles = int((n_rows + kBM - 1) / kBM) + n_experts;
-  uint16_t* h = static_cast<uint16_t*>(workspace);
   auto grid_for = [&](int n_col_tiles) {
-    const int64_t tiles = int64_t(max_m_tiles) * n_col_tiles;
-    return unsigned((tiles + kXcds - 1) / kXcds * kXcds);
+    const int64_t units = int64_t(max_m_tiles) * n_col_tiles + n_cus;
+    return unsigned((units + kXcds - 1) / kXcds * kXcds);
   };
-  // gate/up: F/(kBN/2) column tiles (kBN/2 gate + kBN/2 up rows per B tile), K = D
-  const int nct1 = int((ffn + kBN / 2 - 1) / (kBN / 2));
   auto kernel_for = [](int64_t k, auto k1, auto k2, auto k3) {
     const int64_t stages = k / kBK;
     return stages == 1 ? k1 : (stages % 2 == 0 ? k2 : k3);
   };
+  zero_counters_kernel<<<1, 256, 0, stream>>>(counters, 2 * kCuMax);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // gate/up: F/(kBN/2) column tiles (kBN/2 gate + kBN/2 up rows per B tile), K = D
+  const int nct1 = int((ffn + kBN / 2 - 1) / (kBN / 2));
   kernel_for(hidden, grouped_gemm_kernel<0, 1>, grouped_gemm_kernel<0, 2>,
              grouped_gemm_kernel<0, 3>)<<<grid_for(nct1), kThreads, 0, stream>>>(
       static_cast<const uint16_t*>(rows), n_rows, int(hidden), expert_offsets, n_experts,
       static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), int(ffn), h,
-      int(ffn), nct1);
-  hipError_t err = hipGetLastError();
+      int(ffn), nct1, n_cus, partials, counters);
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   // down: ceil(D/kBN) column tiles, K = F
   const int nct2 = int((hidden + kBN - 1) / kBN);
   kernel_for(ffn, grouped_gemm_kernel<1, 1>, grouped_gemm_kernel<1, 2>,
              grouped_gemm_kernel<1, 3>)<<<grid_for(nct2), kThreads, 0, stream>>>(
       h, n_rows, int(ffn), expert_offsets, n_experts, static_cast<const uint16_t*>(w_down),
-      nullptr, int(hidden), static_cast<uint16_t*>(y), int(hidden), nct2);
+      nullptr, int(hidden), static_cast<uint16_t*>(y), int(hidden), nct2, n_cus, partials,
+      counters + kCuMax);
   return hipGetLastError();
 }
 

@@ -272,7 +272,9 @@ size_t moe_grouped_swiglu_workspace_bytes(int64_t n_rows, int32_t n_experts, int
  *   h = bf16( silu(W_gate[e] r_p) * (W_up[e] r_p) ),  silu(a) = a / (1 + e^-a)
  *   y[p] = bf16( W_down[e] h )
  * bf16 inputs, fp32 accumulation on the matrix cores, h stored as bf16 in the
- * workspace between the two products.
+ * workspace between the two products.  Tiles of a last, partial round of
+ * workgroups are split along K; their fp32 partials (in the workspace) are
+ * summed in a fixed order, so the output is the same on every call.
  *
  *   rows            [n_rows, D] bfloat16, grouped by expert (sorted dispatch)
  *   expert_offsets  [E+1] int32, device-resident (never read by the host);

@@ -130,3 +130,25 @@ def test_grouped_swiglu_offsets_outside_the_contract(offs):
     assert (yy[~inside] == 7.0).all()
     ref = swiglu_rows(rows[inside], experts[inside], wg, wu, wd)
     check_swiglu(to_np(y)[inside], ref, experts[inside], what=f"offsets {offs}")
+
+
+def test_grouped_swiglu_split_tiles_deterministic():
+    """Few tiles over a long K: every tile of both launches is split into K parts
+    (up to 8) whose fp32 partials are summed in part order by the last part to
+    finish.  Parity with the oracle, and bit-identical output on a second call."""
+    rng = np.random.default_rng(8)
+    e, d, f = 3, 1024, 512
+    offs = np.array([0, 130, 130, 300], np.int32)
+    n_rows = int(offs[-1])
+    rows = _bf16(rng.standard_normal((n_rows, d)))
+    wg = _bf16(rng.standard_normal((e, f, d)) * 0.05)
+    wu = _bf16(rng.standard_normal((e, f, d)) * 0.05)
+    wd = _bf16(rng.standard_normal((e, d, f)) * 0.05)
+    args = (to_dev(rows), to_dev(offs), to_dev(wg), to_dev(wu), to_dev(wd))
+    y1 = moe.moe_grouped_swiglu(*args)
+    y2 = moe.moe_grouped_swiglu(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    experts = np.repeat(np.arange(e), np.diff(offs))
+    ref = swiglu_rows(rows, experts, wg, wu, wd)
+    check_swiglu(to_np(y1), ref, experts, what="split tiles")
