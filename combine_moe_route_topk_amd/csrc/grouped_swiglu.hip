@@ -30,7 +30,8 @@
 // loads per lane are spread over the next 32 MFMAs (half over the slice that
 // follows the barrier, half over the next stage's first slice) instead of being
 // issued in one burst: measured on MI355X this cut the mean L2 request latency
-// and made the kernel about 11% faster than with the loads in one group.
+// and made the kernel 4-11% faster (depending on the data) than with the loads
+// in one group.
 // LDS rows are 128 bytes with their 16-byte chunks XOR-swizzled by
 // ((row >> 1) & 7), so the 16 rows one 16-lane phase of a ds_read_b128 reads
 // fall in distinct bank groups; the direct loads write whole 1 KB runs, so the
