@@ -567,7 +567,11 @@ int bits_for(int n) {
 DispatchPlan plan_dispatch(int64_t n_tokens, int n_experts, int k, int n_segments) {
   DispatchPlan p{};
   p.nk = n_tokens * k;
-  int64_t chunk = 1024;
+  // about 64 chunks (more rank workgroups, shorter in-order walks), 256 to 1024
+  // pairs each; beyond a million pairs, about 1024 chunks
+  int64_t chunk = ((p.nk + 63) / 64 + 255) / 256 * 256;
+  if (chunk > 1024) chunk = 1024;
+  if (chunk < 256) chunk = 256;
   if (p.nk > int64_t(1024) * 1024) chunk = ((p.nk + 1023) / 1024 + 255) / 256 * 256;
   p.chunk = int(chunk);
   p.n_chunks = int((p.nk + chunk - 1) / chunk);

@@ -52,6 +52,8 @@ def test_prefill_shape(sort, g):
 
 @pytest.mark.parametrize("n,e,k,g,sort", [
     (3001, 256, 8, 4, 1),      # ragged last 64-token chunk
+    (20000, 64, 4, 1, 1),      # 79 counting chunks
+    (9000, 8, 1, 2, 1),        # k = 1 above the one-workgroup size
     (9000, 8, 2, 1, 1),        # k = 2 above the one-workgroup size
     (500, 1024, 8, 16, 1),     # E = 1024 (16 logits per lane)
     (500, 1024, 8, 16, 0),
