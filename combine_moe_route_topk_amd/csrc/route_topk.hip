@@ -204,10 +204,16 @@ __global__ __launch_bounds__(256) void route_copy_kernel(
 #pragma unroll
   for (int u = 0; u < U; ++u)   // wait for the loads once, before the stores
     asm volatile("" : "+v"(buf[u].x), "+v"(buf[u].y), "+v"(buf[u].z), "+v"(buf[u].w));
-  uint4* dst = rows + t * int64_t(k) * nvec;
+  // non-temporal stores: the copy leaves no dirty lines in L2, so the release
+  // at the end of the launch has little to write back before the next one starts
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4* dst = reinterpret_cast<u32x4*>(rows + t * int64_t(k) * nvec);
   for (int j = 0; j < k; ++j) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) dst[vi[u]] = buf[u];
+    for (int u = 0; u < U; ++u) {
+      const u32x4 o = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+      __builtin_nontemporal_store(o, dst + vi[u]);
+    }
     dst += nvec;
   }
 }
