@@ -32,10 +32,13 @@ def _replay_matches(step, outputs, clobber, reps=4):
             assert np.array_equal(to_np(t), eager[i]), (rep, i)
 
 
-@pytest.mark.parametrize("name,sort", [("decode", 0), ("decode", 1), ("segment", 0), ("segment", 1)])
+@pytest.mark.parametrize("name,sort", [("decode", 0), ("decode", 1), ("segment", 0), ("segment", 1),
+                                       ("prefill", 1), ("mixtral", 1)])
 def test_route_dispatch_replays(name, sort):
     """decode unsorted is the identity layout (routing and row copy in one
-    launch); the other cases take the counting-sort maps."""
+    launch); the other cases take the counting-sort maps (256-pair chunks
+    at the segment-major and Mixtral-like sizes, 512-pair chunks at
+    prefill)."""
     cfg = CONFIGS[name]
     inp = make_inputs(cfg)
     logits, x = to_dev(inp["logits"]), to_dev(inp["x"])
