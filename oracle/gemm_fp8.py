@@ -25,8 +25,10 @@ accumulation of these terms.
 Pins (tests/test_oracle_gemm_fp8.py): a closed form for constant codes and
 power-of-two block scales on a non-square block grid (a transposed scale
 index fails it); exact rational brute force on a tiny case; torch's own
-float8 decode and a float64 matmul as an independent route; the per-expert
-weight selection through ragged offsets, including an empty expert.
+float8 decode and a float64 matmul as an independent route (also for a
+subset of output columns spread over several 128-column blocks); the
+per-expert weight selection through ragged offsets, including an empty
+expert.
 """
 from __future__ import annotations
 
@@ -48,38 +50,44 @@ def _check(rows_q, row_scales, w_q, w_scales):
         raise ValueError("scale shapes")
 
 
-def _expert_product(xq, sx, wq_e, sw_e, absolute=False):
-    """xq [m, K] and wq_e [N, K] as float64 values, sx [m, K/128], sw_e
-    [N/128, K/128] -> float64 [m, N]."""
+def _expert_product(xq, sx, wq_e, sw_e, col_block, absolute=False):
+    """xq [m, K] and wq_e [C, K] (C output columns) as float64 values, sx
+    [m, K/128], sw_e [N/128, K/128], col_block [C]: the 128-column block of
+    each output column (n // 128) -> float64 [m, C]."""
     m, k = xq.shape
-    n = wq_e.shape[0]
-    out = np.zeros((m, n))
+    out = np.zeros((m, wq_e.shape[0]))
     for b in range(k // BLOCK):
-        cols = slice(b * BLOCK, (b + 1) * BLOCK)
-        a, w = xq[:, cols], wq_e[:, cols]
+        ks = slice(b * BLOCK, (b + 1) * BLOCK)
+        a, w = xq[:, ks], wq_e[:, ks]
         if absolute:
             a, w = np.abs(a), np.abs(w)
         partial = a @ w.T                                       # exact in float64
-        scale = np.repeat(sw_e[:, b].astype(np.float64), BLOCK)[None, :] * \
+        scale = sw_e[col_block, b].astype(np.float64)[None, :] * \
             sx[:, b].astype(np.float64)[:, None]
         out += (np.abs(scale) if absolute else scale) * partial
     return out
 
 
-def gemm_fp8_rows(rows_q, row_scales, experts, w_q, w_scales, absolute=False):
-    """float64 y for the given rows; ``experts[i]`` is the expert of row i."""
+def gemm_fp8_rows(rows_q, row_scales, experts, w_q, w_scales, absolute=False, cols=None):
+    """float64 y for the given rows; ``experts[i]`` is the expert of row i.
+
+    ``cols`` (optional) lists the output columns n to evaluate, in the order
+    of the result's columns; by default every column.  Each element is the
+    same sum either way -- only fewer of them are formed, and only the weight
+    rows w[e, n] they need are decoded."""
     rows_q = np.asarray(rows_q, np.uint8)
     row_scales = np.asarray(row_scales, np.float32)
     w_q = np.asarray(w_q, np.uint8)
     w_scales = np.asarray(w_scales, np.float32)
     _check(rows_q, row_scales, w_q, w_scales)
     experts = np.asarray(experts, np.int64)
-    out = np.zeros((rows_q.shape[0], w_q.shape[1]))
+    cols = np.arange(w_q.shape[1]) if cols is None else np.asarray(cols, np.int64)
+    out = np.zeros((rows_q.shape[0], cols.size))
     xq = fp8_bits_to_f64(rows_q)
     for e in np.unique(experts):
         sel = np.nonzero(experts == e)[0]
-        out[sel] = _expert_product(xq[sel], row_scales[sel], fp8_bits_to_f64(w_q[e]), w_scales[e],
-                                   absolute)
+        out[sel] = _expert_product(xq[sel], row_scales[sel], fp8_bits_to_f64(w_q[e][cols]),
+                                   w_scales[e], cols // BLOCK, absolute)
     return out
 
 
@@ -100,10 +108,10 @@ def grouped_gemm_fp8(rows_q, row_scales, offsets, w_q, w_scales):
     return f64_to_bf16_bits(y), y
 
 
-def gemm_fp8_magnitude(rows_q, row_scales, experts, w_q, w_scales):
-    """Sum of the absolute values of every term of y (same rows as
+def gemm_fp8_magnitude(rows_q, row_scales, experts, w_q, w_scales, cols=None):
+    """Sum of the absolute values of every term of y (same rows and columns as
     ``gemm_fp8_rows``)."""
-    return gemm_fp8_rows(rows_q, row_scales, experts, w_q, w_scales, absolute=True)
+    return gemm_fp8_rows(rows_q, row_scales, experts, w_q, w_scales, absolute=True, cols=cols)
 
 
 def gemm_fp8_brute(rows_q, row_scales, experts, w_q, w_scales):

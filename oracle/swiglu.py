@@ -52,6 +52,29 @@ def silu(a: np.ndarray) -> np.ndarray:
     return a / (1.0 + np.exp(-a))
 
 
+def _hidden_bits(x_f64: np.ndarray, wg_bf16: np.ndarray, wu_bf16: np.ndarray) -> np.ndarray:
+    """h = bf16(silu(W_gate x) * (W_up x)) for the rows of x (one expert)."""
+    wg = bf16_bits_to_f32(wg_bf16).astype(np.float64)
+    wu = bf16_bits_to_f32(wu_bf16).astype(np.float64)
+    return f64_to_bf16_bits(silu(x_f64 @ wg.T) * (x_f64 @ wu.T))
+
+
+def swiglu_hidden(rows_bf16: np.ndarray, experts: np.ndarray, w_gate_bf16, w_up_bf16) -> np.ndarray:
+    """The hidden activation h [M, F] (uint16 bf16 bits) between the two
+    products, for rows with their experts; rows whose expert lies outside
+    [0, E) give zeros.  The same h that swiglu_rows multiplies by W_down."""
+    r = bf16_bits_to_f32(rows_bf16).astype(np.float64)
+    experts = np.asarray(experts, dtype=np.int64)
+    w_gate = np.asarray(w_gate_bf16)
+    out = np.zeros((r.shape[0], w_gate.shape[1]), dtype=np.uint16)
+    for e in np.unique(experts):
+        if e < 0 or e >= w_gate.shape[0]:
+            continue
+        sel = np.nonzero(experts == e)[0]
+        out[sel] = _hidden_bits(r[sel], w_gate[e], w_up_bf16[e])
+    return out
+
+
 def swiglu_rows_f64(rows_bf16: np.ndarray, experts: np.ndarray, w_gate_bf16, w_up_bf16,
                     w_down_bf16) -> np.ndarray:
     """float64 [M, D] value of y before its final rounding (h is rounded to
@@ -65,12 +88,8 @@ def swiglu_rows_f64(rows_bf16: np.ndarray, experts: np.ndarray, w_gate_bf16, w_u
         if e < 0 or e >= n_exp:
             continue
         sel = np.nonzero(experts == e)[0]
-        wg = bf16_bits_to_f32(w_gate_bf16[e]).astype(np.float64)
-        wu = bf16_bits_to_f32(w_up_bf16[e]).astype(np.float64)
+        h = bf16_bits_to_f32(_hidden_bits(r[sel], w_gate_bf16[e], w_up_bf16[e])).astype(np.float64)
         wd = bf16_bits_to_f32(w_down_bf16[e]).astype(np.float64)
-        x = r[sel]
-        h_bits = f64_to_bf16_bits(silu(x @ wg.T) * (x @ wu.T))
-        h = bf16_bits_to_f32(h_bits).astype(np.float64)
         out[sel] = h @ wd.T
     return out
 

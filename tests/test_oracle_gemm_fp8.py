@@ -67,6 +67,15 @@ def test_matches_torch_decode_and_matmul():
         assert np.allclose(got[p], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
     mag = gemm_fp8_magnitude(rows, sx, experts, w, sw)
     assert (mag >= np.abs(got) * (1 - 1e-12)).all()
+    # a subset of output columns spread over both 128-column blocks, out of order:
+    # each column keeps its own block's weight scale
+    cols = np.array([255, 0, 127, 128, 200, 3])
+    sub = gemm_fp8_rows(rows, sx, experts, w, sw, cols=cols)
+    for p in range(6):
+        wd = dec(w[experts[p]]) * np.repeat(np.repeat(sw[experts[p]].astype(np.float64), 128, 0), 128, 1)
+        want = (wd @ xd[p])[cols]
+        assert np.allclose(sub[p], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    assert np.array_equal(gemm_fp8_magnitude(rows, sx, experts, w, sw, cols=cols), mag[:, cols])
 
 
 def test_ragged_offsets_pick_each_rows_expert():

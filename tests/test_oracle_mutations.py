@@ -199,7 +199,7 @@ from tests import test_oracle_gemm_fp8 as tg
 
 
 def _product_mutant(kind):
-    def f(xq, sx, wq_e, sw_e, absolute=False):
+    def f(xq, sx, wq_e, sw_e, col_block, absolute=False):
         m, k = xq.shape
         nb = k // og.BLOCK
         out = np.zeros((m, wq_e.shape[0]))
@@ -211,7 +211,7 @@ def _product_mutant(kind):
             else:
                 col_scale = sw_e[:, b]
             row_scale = sx[:, (b + 1) % nb] if kind == "row_scale_next_block" else sx[:, b]
-            scale = np.repeat(col_scale.astype(np.float64), og.BLOCK)[None, :] * \
+            scale = col_scale.astype(np.float64)[col_block][None, :] * \
                 row_scale.astype(np.float64)[:, None]
             out += scale * partial
         return out

@@ -4,8 +4,8 @@ import math
 import numpy as np
 
 from oracle import codecs, dispatch as od
-from oracle.swiglu import (grouped_swiglu, silu, swiglu_brute, swiglu_combine, swiglu_rows,
-                           swiglu_rows_f64)
+from oracle.swiglu import (_bf16_round_py, grouped_swiglu, silu, swiglu_brute, swiglu_combine,
+                           swiglu_hidden, swiglu_rows, swiglu_rows_f64)
 
 
 def _bf16(a):
@@ -35,6 +35,36 @@ def test_rows_match_pure_python_brute_force():
         # h is rounded to bf16 on both sides; a 1-ulp flip of one h element can
         # move y by much less than a bf16 ulp, so compare within one ulp
         assert np.all(np.abs(got[p] - ref_b) <= np.abs(ref_b) * 2**-7 + 1e-30), p
+
+
+def test_hidden_matches_brute_force_and_feeds_the_down_product():
+    """h on its own: each element against a pure-Python fsum of the gate and
+    up dot products, silu by math.exp and the scaling RNE of swiglu_brute; then
+    h times W_down (float64) rounded once must be swiglu_rows exactly."""
+    rng = np.random.default_rng(7)
+    e, f, d = 3, 9, 6
+    wg, wu = _bf16(rng.standard_normal((e, f, d)) * 0.5), _bf16(rng.standard_normal((e, f, d)) * 0.5)
+    wd = _bf16(rng.standard_normal((e, d, f)) * 0.5)
+    rows = _bf16(rng.standard_normal((8, d)))
+    experts = np.array([1, 2, 0, 1, -1, 2, 2, 0])
+    h = swiglu_hidden(rows, experts, wg, wu)
+    assert h.shape == (8, f)
+    assert (h[4] == 0).all()                            # bad id: no row
+    dec = lambda b: codecs.bf16_bits_to_f32(b).astype(np.float64).tolist()
+    for p, ex in enumerate(experts):
+        if ex < 0:
+            continue
+        r = dec(rows[p])
+        for i in range(f):
+            g = math.fsum(a * b for a, b in zip(dec(wg[ex][i]), r))
+            u = math.fsum(a * b for a, b in zip(dec(wu[ex][i]), r))
+            want = _bf16_round_py(g / (1.0 + math.exp(-g)) * u)
+            assert float(codecs.bf16_bits_to_f32(h[p:p + 1, i])[0]) == want, (p, i)
+    ok = experts >= 0
+    hf = codecs.bf16_bits_to_f32(h[ok]).astype(np.float64)
+    y = np.stack([hf[i] @ codecs.bf16_bits_to_f32(wd[ex]).astype(np.float64).T
+                  for i, ex in enumerate(experts[ok])])
+    assert np.array_equal(codecs.f64_to_bf16_bits(y), swiglu_rows(rows[ok], experts[ok], wg, wu, wd))
 
 
 def test_unit_case_two_rows_on_one_expert():
