@@ -47,9 +47,59 @@ def _need(t: torch.Tensor, name: str, dtypes, device=None) -> None:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _shape(t: Optional[torch.Tensor], name: str, shape) -> None:
+    """The kernels take raw pointers: every buffer must hold exactly the
+    elements the C call will touch, so undersized tensors are rejected here,
+    before any launch."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_dispatch_out(out: "DispatchResult", n: int, k: int, n_experts: int, n_segments: int,
+                        x: Optional[torch.Tensor], x_scales: Optional[torch.Tensor], dev) -> None:
+    nk = n * k
+    for name, shape in (("expert_counts", (n_experts,)), ("expert_offsets", (n_experts + 1,)),
+                        ("segment_offsets", (n_segments + 1,)), ("src_pair", (nk,)),
+                        ("dst_pos", (nk,))):
+        t = getattr(out, name)
+        _need(t, f"out.{name}", (torch.int32,), dev)
+        _shape(t, f"out.{name}", shape)
+    if out.row_expert is not None:
+        _need(out.row_expert, "out.row_expert", (torch.int32,), dev)
+        _shape(out.row_expert, "out.row_expert", (nk,))
+    if (x is None) != (out.rows is None):
+        raise ValueError("out.rows must be given exactly when x is")
+    if x is not None:
+        _need(out.rows, "out.rows", (x.dtype,), dev)
+        _shape(out.rows, "out.rows", (nk, x.shape[1]))
+    if (x_scales is None) != (out.row_scales is None):
+        raise ValueError("out.row_scales must be given exactly when x_scales is")
+    if x_scales is not None:
+        _need(out.row_scales, "out.row_scales", (torch.float32,), dev)
+        _shape(out.row_scales, "out.row_scales", (nk, x_scales.shape[1]))
+
+
 _PAYLOAD = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.uint8: MOE_F8E4M3,
             torch.float8_e4m3fn: MOE_F8E4M3}
 _FLOAT_IO = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+
+def _payload_args(x, x_scales, n: int, dev):
+    """(dtype code, hidden) of a dispatch payload, with its shape checks."""
+    if x is None:
+        if x_scales is not None:
+            raise ValueError("x_scales given without x")
+        return MOE_BF16, 1
+    _need(x, "x", tuple(_PAYLOAD), dev)
+    if x.dim() != 2 or x.shape[0] != n:
+        raise ValueError(f"x must be [N={n}, D]")
+    hidden = x.shape[1]
+    if x_scales is not None:
+        _need(x_scales, "x_scales", (torch.float32,), dev)
+        if hidden % 128:
+            raise ValueError("an fp8 payload needs D % 128 == 0")
+        _shape(x_scales, "x_scales", (n, hidden // 128))
+    return _PAYLOAD[x.dtype], hidden
 
 
 def moe_abi_version() -> int:
@@ -61,6 +111,8 @@ def moe_route_topk(logits: torch.Tensor, k: int, renormalize: bool = True,
                    stream=None):
     """logits [N, E] float32 -> (topk_idx [N, k] int32, topk_w [N, k] float32)."""
     _need(logits, "logits", (torch.float32,))
+    if logits.dim() != 2:
+        raise ValueError("logits must be [N, E]")
     n, e = logits.shape
     if topk_idx is None:
         topk_idx = torch.empty((n, k), dtype=torch.int32, device=logits.device)
@@ -109,18 +161,12 @@ def moe_dispatch(x: Optional[torch.Tensor], topk_idx: torch.Tensor, n_experts: i
     [N, D/128] float32), or None to compute the maps only.  ``out`` may carry
     preallocated outputs (reused in place)."""
     _need(topk_idx, "topk_idx", (torch.int32,))
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [N, k]")
     dev = topk_idx.device
     n, k = topk_idx.shape
     nk = n * k
-    if x is not None:
-        _need(x, "x", tuple(_PAYLOAD), dev)
-        if x.shape[0] != n:
-            raise ValueError("x and topk_idx disagree on N")
-        dtype, hidden = _PAYLOAD[x.dtype], x.shape[1]
-    else:
-        dtype, hidden = MOE_BF16, 1
-    if x_scales is not None:
-        _need(x_scales, "x_scales", (torch.float32,), dev)
+    dtype, hidden = _payload_args(x, x_scales, n, dev)
     if out is None:
         i32 = dict(dtype=torch.int32, device=dev)
         rows = None if x is None else torch.empty((nk, hidden), dtype=x.dtype, device=dev)
@@ -129,6 +175,7 @@ def moe_dispatch(x: Optional[torch.Tensor], topk_idx: torch.Tensor, n_experts: i
                              torch.empty(n_segments + 1, **i32), torch.empty(nk, **i32),
                              torch.empty(nk, **i32),
                              torch.empty(nk, **i32) if want_row_expert else None, rows, rs)
+    _check_dispatch_out(out, n, k, n_experts, n_segments, x, x_scales, dev)
     if workspace is None:
         wsb = moe_dispatch_workspace_bytes(n, n_experts, k, n_segments)
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
@@ -159,6 +206,8 @@ def moe_route_dispatch(logits: torch.Tensor, x: Optional[torch.Tensor], k: int,
                        stream=None):
     """Routing and dispatch in one call -> (topk_idx, topk_w, DispatchResult)."""
     _need(logits, "logits", (torch.float32,))
+    if logits.dim() != 2:
+        raise ValueError("logits must be [N, E]")
     dev = logits.device
     n, e = logits.shape
     nk = n * k
@@ -168,15 +217,9 @@ def moe_route_dispatch(logits: torch.Tensor, x: Optional[torch.Tensor], k: int,
         topk_w = torch.empty((n, k), dtype=torch.float32, device=dev)
     _need(topk_idx, "topk_idx", (torch.int32,), dev)
     _need(topk_w, "topk_w", (torch.float32,), dev)
-    if x is not None:
-        _need(x, "x", tuple(_PAYLOAD), dev)
-        if x.shape[0] != n:
-            raise ValueError("x and logits disagree on N")
-        dtype, hidden = _PAYLOAD[x.dtype], x.shape[1]
-    else:
-        dtype, hidden = MOE_BF16, 1
-    if x_scales is not None:
-        _need(x_scales, "x_scales", (torch.float32,), dev)
+    _shape(topk_idx, "topk_idx", (n, k))
+    _shape(topk_w, "topk_w", (n, k))
+    dtype, hidden = _payload_args(x, x_scales, n, dev)
     if out is None:
         i32 = dict(dtype=torch.int32, device=dev)
         rows = None if x is None else torch.empty((nk, hidden), dtype=x.dtype, device=dev)
@@ -185,6 +228,7 @@ def moe_route_dispatch(logits: torch.Tensor, x: Optional[torch.Tensor], k: int,
                              torch.empty(n_segments + 1, **i32), torch.empty(nk, **i32),
                              torch.empty(nk, **i32),
                              torch.empty(nk, **i32) if want_row_expert else None, rows, rs)
+    _check_dispatch_out(out, n, k, e, n_segments, x, x_scales, dev)
     if workspace is None:
         wsb = moe_route_dispatch_workspace_bytes(n, e, k, n_segments)
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
@@ -212,6 +256,8 @@ def moe_scatter_rows(x: torch.Tensor, dst_pos: torch.Tensor, k: int,
     _need(rows, "rows", (x.dtype,), x.device)
     if dst_pos.numel() != n * k or rows.shape[0] != n * k:
         raise ValueError("dst_pos and rows must hold N*k entries")
+    if tuple(rows.shape[1:]) != tuple(x.shape[1:]):
+        raise ValueError("rows must have the row shape of x")
     check("moe_scatter_rows", lib.moe_scatter_rows(_ptr(x), n, row_bytes, k, _ptr(dst_pos),
                                                    _ptr(rows), _stream(stream)))
     return rows
@@ -228,6 +274,7 @@ def moe_gather_rows(x: torch.Tensor, src_pair: torch.Tensor, k: int,
     if rows is None:
         rows = torch.empty((n_rows,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
     _need(rows, "rows", (x.dtype,), x.device)
+    _shape(rows, "rows", (n_rows,) + tuple(x.shape[1:]))
     check("moe_gather_rows", lib.moe_gather_rows(_ptr(x), n, row_bytes, k, _ptr(src_pair), n_rows,
                                                  _ptr(rows), _stream(stream)))
     return rows
@@ -241,6 +288,8 @@ def moe_combine(y: torch.Tensor, dst_pos: torch.Tensor, topk_w: torch.Tensor,
     dev = y.device
     _need(dst_pos, "dst_pos", (torch.int32,), dev)
     _need(topk_w, "topk_w", (torch.float32,), dev)
+    if topk_w.dim() != 2 or y.dim() != 2:
+        raise ValueError("topk_w must be [N, k] and y [N*k, D]")
     n, k = topk_w.shape
     hidden = y.shape[1]
     if dst_pos.numel() != n * k or y.shape[0] != n * k:
@@ -248,6 +297,7 @@ def moe_combine(y: torch.Tensor, dst_pos: torch.Tensor, topk_w: torch.Tensor,
     if out is None:
         out = torch.empty((n, hidden), dtype=out_dtype or y.dtype, device=dev)
     _need(out, "out", tuple(_FLOAT_IO), dev)
+    _shape(out, "out", (n, hidden))
     check("moe_combine", lib.moe_combine(_ptr(y), _FLOAT_IO[y.dtype], n, hidden, k, _ptr(dst_pos),
                                          _ptr(topk_w), _ptr(out), _FLOAT_IO[out.dtype],
                                          _stream(stream)))
@@ -259,10 +309,14 @@ def moe_dequant_rows(rows: torch.Tensor, row_scales: torch.Tensor,
     """fp8 E4M3FN rows [R, D] (uint8 or float8_e4m3fn) + scales [R, D/128] -> bf16 [R, D]."""
     _need(rows, "rows", (torch.uint8, torch.float8_e4m3fn))
     _need(row_scales, "row_scales", (torch.float32,), rows.device)
+    if rows.dim() != 2 or rows.shape[1] % 128:
+        raise ValueError("rows must be [R, D] with D % 128 == 0")
     r, d = rows.shape
+    _shape(row_scales, "row_scales", (r, d // 128))
     if out is None:
         out = torch.empty((r, d), dtype=torch.bfloat16, device=rows.device)
     _need(out, "out", (torch.bfloat16,), rows.device)
+    _shape(out, "out", (r, d))
     check("moe_dequant_rows", lib.moe_dequant_rows(_ptr(rows), _ptr(row_scales), r, d, _ptr(out),
                                                    _stream(stream)))
     return out
@@ -281,8 +335,14 @@ def moe_grouped_swiglu(rows: torch.Tensor, expert_offsets: torch.Tensor, w_gate:
     for name, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
         _need(t, name, (torch.bfloat16,), dev)
     _need(expert_offsets, "expert_offsets", (torch.int32,), dev)
+    if rows.dim() != 2 or w_gate.dim() != 3:
+        raise ValueError("moe_grouped_swiglu: rows must be [R, D] and w_gate [E, F, D]")
     r, d = rows.shape
-    e, f, _ = w_gate.shape
+    e, f, d2 = w_gate.shape
+    if d2 != d or tuple(w_up.shape) != (e, f, d) or tuple(w_down.shape) != (e, d, f) or \
+            expert_offsets.numel() != e + 1:
+        raise ValueError("moe_grouped_swiglu: inconsistent shapes (w_gate, w_up [E, F, D], "
+                         "w_down [E, D, F], expert_offsets [E+1])")
     if y is None:
         y = torch.empty_like(rows)
     _need(y, "y", (torch.bfloat16,), dev)

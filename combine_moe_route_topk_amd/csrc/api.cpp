@@ -255,6 +255,8 @@ int moe_scatter_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int32_t
                      const int32_t* dst_pos, void* rows, void* stream) {
   const char* fn = "moe_scatter_rows";
   if (n_tokens < 0 || row_bytes < 1 || k < 1) return fail(MOE_ERR_ARG, "%s: need n_tokens >= 0, row_bytes >= 1, k >= 1", fn);
+  // one lane of a wave holds each of a token's k destinations
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "%s: k > %d", fn, MOE_MAX_TOPK);
   if (n_tokens * int64_t(k) > INT32_MAX)
     return fail(MOE_ERR_UNSUPPORTED, "%s: n_tokens * k exceeds the int32 index range", fn);
   if (n_tokens == 0) return ok();

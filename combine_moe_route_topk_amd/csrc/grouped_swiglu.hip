@@ -52,6 +52,8 @@
 // kernel at the start of every call); the part that arrives last sums the
 // partials in part order, so the result does not depend on which part that
 // was, and writes the tile.  Nothing waits on another workgroup.
+#include <atomic>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -524,14 +526,25 @@ __global__ void zero_counters_kernel(int32_t* __restrict__ c, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) c[i] = 0;
 }
 
-// CUs of the current device, as a multiple of kXcds in [kXcds, kCuMax].
+// CUs of the current device, as a multiple of kXcds in [kXcds, kCuMax],
+// queried once per device and kept (a racing first call stores the same value).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
 int cu_count() {
-  int dev = 0, n = kCuMax;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = kCuMax;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     n = kCuMax;
   n = n / kXcds * kXcds;
-  return n < kXcds ? kXcds : (n > kCuMax ? kCuMax : n);
+  n = n < kXcds ? kXcds : (n > kCuMax ? kCuMax : n);
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 }  // namespace

@@ -55,6 +55,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
 }
 
+// exp(a - b) without the rounding error of the fp32 difference.  Knuth's
+// two-sum splits a - b exactly into s + r with s = fl(a - b) and |r| <= ulp(s)/2;
+// then exp(a - b) = exp(s) * exp(r) = exp(s) * (1 + r) to far below fp32
+// precision.  A plain expf(a - b) would carry the difference's relative error
+// times |a - b| into the result (up to ~5e-6 relative at |a - b| ~ 80).
+__device__ __forceinline__ float exp_diff(float a, float b) {
+  const float c = -b;
+  const float s = a + c;
+  const float cc = s - a;
+  const float r = (a - (s - cc)) + (c - cc);
+  const float e = expf(s);
+  return fmaf(e, r, e);
+}
+
 __device__ __forceinline__ int wave_min_i32(int v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -122,7 +136,7 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
   }
 
   const float top = __shfl(my_v, 0);                  // slot 0 is the maximum
-  const float num = lane < k ? expf(my_v - top) : 0.f;
+  const float num = lane < k ? exp_diff(my_v, top) : 0.f;
   float den;
   if (renormalize) {
     den = wave_reduce_sum(num);
@@ -130,7 +144,7 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (lane + r * kWave < n_experts) s += expf(val[r] - top);
+      if (lane + r * kWave < n_experts) s += exp_diff(val[r], top);
     den = wave_reduce_sum(s);
   }
   out_e = my_e;

@@ -213,7 +213,8 @@ int moe_route_dispatch(const float* logits, int32_t renormalize, int32_t* topk_i
  *   rows [N*k, row_bytes], output; entries of dst_pos outside [0, N*k) are
  *   skipped.
  * Errors: MOE_ERR_ARG for null pointers (unless N == 0), N < 0,
- * row_bytes < 1, k < 1; MOE_ERR_UNSUPPORTED for N*k > INT32_MAX. */
+ * row_bytes < 1, k < 1; MOE_ERR_UNSUPPORTED for k > MOE_MAX_TOPK or
+ * N*k > INT32_MAX. */
 int moe_scatter_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int32_t k,
                      const int32_t* dst_pos, void* rows, void* stream);
 

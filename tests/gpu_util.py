@@ -6,7 +6,9 @@ The tolerances follow from the arithmetic:
 * bf16 combine output: within one bf16 ulp of the correctly rounded exact
   value, or, where the terms cancel, within the fp32 bound plus half a bf16
   ulp of the result;
-* routing weights: 1e-6 relative (a handful of fp32 roundings plus expf);
+* routing weights: 1e-6 relative, with no absolute slack above the fp32
+  normal range (W_ATOL = 2^-126, the smallest normal: below it fp32 keeps
+  fewer than 24 significant bits); a handful of fp32 roundings plus expf;
 * SwiGLU expert FFN (bf16 inputs, fp32 accumulation, h rounded to bf16 on
   both sides): every element within 2e-2 * max(|o|, rms of its row), and each
   expert's relative Frobenius error within 2e-2.  A flipped bf16 rounding of
@@ -21,6 +23,7 @@ import torch
 from oracle import codecs
 
 DEV = "cuda:0"
+W_ATOL = 2.0 ** -126          # routing weights: absolute floor only below the fp32 normal range
 
 
 def to_dev(a: np.ndarray, kind: str | None = None) -> torch.Tensor:
@@ -89,3 +92,64 @@ def check_swiglu(got_bits, ref_bits, experts, what=""):
         sel = experts == e
         rel = np.linalg.norm(g[sel] - o[sel]) / max(np.linalg.norm(o[sel]), 1e-30)
         assert rel <= 2e-2, f"{what}: expert {e} relative error {rel:.3e}"
+
+
+def check_weights(got: np.ndarray, want: np.ndarray, what: str = "") -> None:
+    """Routing weights at 1e-6 relative (absolute floor only for subnormals)."""
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=W_ATOL, err_msg=what)
+
+
+def tile_rows(offsets, tile: int, rng) -> np.ndarray:
+    """Rows to check in a grouped buffer: one random row from every `tile`-row
+    tile of every expert (tiles start at the expert's first row, as the
+    grouped kernels cut them), plus each non-empty expert's last row."""
+    offs = np.asarray(offsets, dtype=np.int64)
+    picks = []
+    for e in range(offs.size - 1):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        for t0 in range(lo, hi, tile):
+            picks.append(int(rng.integers(t0, min(t0 + tile, hi))))
+        if hi > lo:
+            picks.append(hi - 1)
+    return np.unique(np.array(picks, dtype=np.int64))
+
+
+def combine_check_all_tokens(out_dev, y_dev, dst_pos_dev, w_dev, k: int, out_bf16: bool,
+                             what: str = "", chunk: int = 512) -> None:
+    """Every token of a full-size combine against the float64 oracle, in token
+    chunks (the oracle evaluates each token on its own)."""
+    y = as_f32(to_np(y_dev))
+    dst, w = to_np(dst_pos_dev), to_np(w_dev)
+    got = to_np(out_dev)
+    n = w.shape[0]
+    for t0 in range(0, n, chunk):
+        toks = np.arange(t0, min(t0 + chunk, n))
+        exact, mag = combine_reference(y, dst, w, k, tokens=toks)
+        check_combine(got[toks], exact, mag, out_bf16, what=f"{what} tokens {t0}..")
+
+
+def per_expert_oracle(fn, experts: np.ndarray, fetch, workers: int = 8):
+    """Evaluate an oracle function expert by expert on a thread pool.
+
+    experts: the expert of each selected row; fetch(e) -> the expert's host
+    operands; fn(row_indices, local_expert_ids, operands) -> result rows.
+    Returns the results stacked in the order of `experts`."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    experts = np.asarray(experts)
+    uniq = np.unique(experts)
+
+    def one(e):
+        sel = np.nonzero(experts == e)[0]
+        return sel, fn(sel, np.zeros(sel.size, np.int64), fetch(int(e)))
+
+    from threadpoolctl import threadpool_limits
+
+    out = None
+    # one BLAS thread per worker: nested BLAS pools oversubscribe the cores
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as pool:
+        for sel, res in pool.map(one, uniq):
+            if out is None:
+                out = np.zeros((experts.size,) + res.shape[1:], dtype=res.dtype)
+            out[sel] = res
+    return out

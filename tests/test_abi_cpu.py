@@ -158,6 +158,9 @@ def test_row_copy_errors():
     assert s(FAKE, 4, 16, 0, FAKE, FAKE, None) == ARG
     assert s(None, 4, 16, 2, FAKE, FAKE, None) == ARG
     assert s(FAKE, 2**30, 16, 4, FAKE, FAKE, None) == UNSUP
+    assert s(FAKE, 4, 16, 65, FAKE, FAKE, None) == UNSUP     # k above MOE_MAX_TOPK
+    assert b"k > 64" in lib.moe_last_error()
+    assert s(FAKE, 0, 16, 65, None, None, None) == UNSUP     # checked before the N == 0 no-op
     assert s(None, 0, 16, 2, None, None, None) == 0
     assert g(FAKE, 4, 16, 2, FAKE, -1, FAKE, None) == ARG
     assert g(FAKE, 4, 16, 2, None, 8, FAKE, None) == ARG

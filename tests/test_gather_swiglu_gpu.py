@@ -9,7 +9,8 @@ import combine_moe_route_topk_amd as moe
 from oracle import codecs
 from oracle.combine import combine_f64
 from oracle.swiglu import swiglu_combine, swiglu_rows
-from tests.gpu_util import DEV, check_combine, check_swiglu, to_dev, to_np
+from tests.gpu_util import (DEV, check_swiglu, combine_check_all_tokens, per_expert_oracle, to_dev,
+                            to_np)
 from workloads import DECODE_FFN, make_inputs, make_swiglu_weights_device
 
 pytestmark = pytest.mark.gpu
@@ -94,9 +95,9 @@ def test_gather_swiglu_deterministic_and_empty():
 def test_decode_layer_with_experts_full_size():
     """Decode with real experts: N=128, D=7168, E=256, top-8, unsorted identity
     layout, F=2048.  Route + unsorted dispatch -> per-row SwiGLU reading the
-    rows where the dispatch left them -> combine.  Sampled rows of 8 experts
-    are checked against the oracle; the combine is checked on the GPU's own y
-    for 16 tokens."""
+    rows where the dispatch left them -> combine.  Every row (all active
+    experts) is checked against the oracle, each expert's weights copied back
+    in turn; the combine is checked on every token on the GPU's own y."""
     cfg = DECODE_FFN
     inp = make_inputs(cfg)
     w = make_swiglu_weights_device(cfg)
@@ -108,20 +109,15 @@ def test_decode_layer_with_experts_full_size():
     torch.cuda.synchronize()
     rexp = to_np(res.row_expert)
     assert np.array_equal(rexp, to_np(idx).reshape(-1))     # identity layout: row t*k+j
-    rng = np.random.default_rng(0)
-    chosen = np.sort(rng.choice(np.unique(rexp), 8, replace=False))
-    sample = np.nonzero(np.isin(rexp, chosen))[0]
-    sel = torch.from_numpy(chosen).to(DEV)
-    host = {k: v.index_select(0, sel).view(torch.int16).cpu().numpy().view(np.uint16)
-            for k, v in w.items()}
-    local = np.searchsorted(chosen, rexp[sample])
-    ref = swiglu_rows(to_np(res.rows)[sample], local, host["w_gate"], host["w_up"], host["w_down"])
-    check_swiglu(to_np(y)[sample], ref, local, what="decode experts")
-    yf = codecs.bf16_bits_to_f32(to_np(y))
-    toks = rng.choice(cfg.n_tokens, 16, replace=False)
-    exact = combine_f64(yf, to_np(res.dst_pos), to_np(tw), cfg.top_k, tokens=toks)
-    mag = combine_f64(np.abs(yf), to_np(res.dst_pos), np.abs(to_np(tw)), cfg.top_k, tokens=toks)
-    check_combine(to_np(out)[toks], exact, mag, True, what="decode combine")
+    rows = to_np(res.rows)
+
+    def fetch(e):
+        return [w[nm][e:e + 1].view(torch.int16).cpu().numpy().view(np.uint16)
+                for nm in ("w_gate", "w_up", "w_down")]
+
+    ref = per_expert_oracle(lambda sel, local, ops: swiglu_rows(rows[sel], local, *ops), rexp, fetch)
+    check_swiglu(to_np(y), ref, rexp, what="decode experts, every row")
+    combine_check_all_tokens(out, y, res.dst_pos, tw, cfg.top_k, True, what="decode combine")
 
 
 def test_gather_swiglu_multi_workgroup_grouping():

@@ -23,7 +23,7 @@ import torch
 import combine_moe_route_topk_amd as moe
 from oracle import codecs
 from oracle.gemm_fp8 import gemm_fp8_magnitude, gemm_fp8_rows
-from tests.gpu_util import DEV, to_dev, to_np
+from tests.gpu_util import DEV, per_expert_oracle, tile_rows, to_dev, to_np
 from workloads import CONFIGS, FP8_GEMM_N, make_fp8_expert_weights_device, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -99,8 +99,10 @@ def test_grouped_gemm_fp8_deterministic():
 def test_segment_workload_fp8_projection_full_size():
     """Segment-major workload (N=1024 tokens, D=7168 fp8 + 1x128 scales, E=256,
     top-8): routing, the sorted fp8 dispatch, then the fp8 grouped projection
-    (N_out = 4096) reading the dispatched rows and scales in place; sampled
-    rows from 8 experts checked against the oracle."""
+    (N_out = 4096) reading the dispatched rows and scales in place.  Checked
+    against the oracle on every output tile: one row of every 64-row tile of
+    every expert plus each expert's last row, at four columns of every
+    128-column tile (its first and last and two random ones)."""
     cfg = CONFIGS["segment"]
     inp = make_inputs(cfg)
     x = to_dev(inp["x"])
@@ -115,16 +117,25 @@ def test_segment_workload_fp8_projection_full_size():
     assert tuple(y.shape) == (cfg.n_tokens * cfg.top_k, FP8_GEMM_N)
     offs = to_np(res.expert_offsets)
     rng = np.random.default_rng(0)
-    busy = [ex for ex in range(cfg.n_experts) if offs[ex + 1] > offs[ex]]
-    chosen = sorted(rng.choice(busy, 8, replace=False))
-    sample, experts = [], []
-    for j, ex in enumerate(chosen):
-        picks = sorted(set(rng.integers(offs[ex], offs[ex + 1], 2)) | {offs[ex + 1] - 1})
-        sample += picks
-        experts += [j] * len(picks)
-    sample = np.array(sample)
-    idx_t = torch.from_numpy(np.array(chosen)).to(DEV)
-    w_host = wt["w"].index_select(0, idx_t).cpu().numpy()
-    sw_host = wt["w_scales"].index_select(0, idx_t).cpu().numpy()
-    check_fp8_gemm(to_np(y)[sample], to_np(res.rows)[sample], to_np(res.row_scales)[sample],
-                   np.array(experts), w_host, sw_host, "segment fp8 projection")
+    sample = tile_rows(offs, 64, rng)
+    experts = to_np(res.row_expert)[sample]
+    cols = np.concatenate([np.unique(np.concatenate([[c, c + 127], c + rng.integers(1, 127, 2)]))
+                           for c in range(0, FP8_GEMM_N, 128)])
+    rows_s, sx_s, got = to_np(res.rows)[sample], to_np(res.row_scales)[sample], to_np(y)[sample][:, cols]
+
+    def fetch(e):
+        return wt["w"][e:e + 1].cpu().numpy(), wt["w_scales"][e:e + 1].cpu().numpy()
+
+    def oracle(sel, local, ops):
+        w_e, sw_e = ops
+        return np.stack([gemm_fp8_rows(rows_s[sel], sx_s[sel], local, w_e, sw_e, cols=cols),
+                         gemm_fp8_magnitude(rows_s[sel], sx_s[sel], local, w_e, sw_e, cols=cols)])
+
+    both = per_expert_oracle(lambda sel, local, ops: oracle(sel, local, ops).transpose(1, 0, 2),
+                             experts, fetch)
+    exact, mag = both[:, 0], both[:, 1]
+    g = codecs.bf16_bits_to_f32(got).astype(np.float64)
+    err = np.abs(g - exact)
+    bad = err > 2.0 ** -8 * np.abs(exact) + 2.0 ** -11 * mag
+    assert not bad.any(), f"segment fp8 projection: {bad.sum()} of {bad.size} outside the bound"
+    assert len(np.unique(experts)) == int(np.sum(np.diff(offs) > 0))     # every busy expert

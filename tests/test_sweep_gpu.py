@@ -7,7 +7,7 @@ import torch
 import combine_moe_route_topk_amd as moe
 from oracle import codecs, dispatch as od
 from oracle.route import route_topk as oracle_route
-from tests.gpu_util import as_f32, check_combine, combine_reference, to_dev, to_np
+from tests.gpu_util import as_f32, check_combine, check_weights, combine_reference, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,7 @@ def test_random_shapes(seed):
         return
     oi, ow = oracle_route(logits, k)
     assert np.array_equal(to_np(idx), oi)
-    np.testing.assert_allclose(to_np(w), ow, rtol=1e-6, atol=1e-7)
+    check_weights(to_np(w), ow)
     assert res.sorted == od.resolve_sorted(sort, n, cutoff)
     ref = od.dispatch(oi, e, g, res.sorted, x=x)
     for name in ("expert_counts", "expert_offsets", "segment_offsets", "src_pair", "dst_pos", "row_expert"):
@@ -77,11 +77,12 @@ def test_dispatch_beyond_a_million_pairs(sort, g):
     assert np.array_equal(rows[sample], x[ref["src_pair"][sample] // k])
 
 
-def test_route_many_tokens():
+@pytest.mark.parametrize("renorm", [True, False])
+def test_route_many_tokens(renorm):
     rng = np.random.default_rng(12)
     logits = rng.standard_normal((50_000, 256)).astype(np.float32)
-    idx, w = moe.moe_route_topk(to_dev(logits), 8)
+    idx, w = moe.moe_route_topk(to_dev(logits), 8, renorm)
     torch.cuda.synchronize()
-    oi, ow = oracle_route(logits, 8)
+    oi, ow = oracle_route(logits, 8, renorm)
     assert np.array_equal(to_np(idx), oi)
-    np.testing.assert_allclose(to_np(w), ow, rtol=1e-6, atol=1e-7)
+    check_weights(to_np(w), ow)

@@ -6,9 +6,8 @@ import torch
 
 import combine_moe_route_topk_amd as moe
 from oracle import codecs, dispatch as od
-from oracle.combine import combine_f64
-from oracle.swiglu import swiglu_rows
-from tests.gpu_util import DEV, check_combine, check_swiglu, to_dev, to_np
+from oracle.swiglu import swiglu_hidden, swiglu_rows
+from tests.gpu_util import DEV, check_swiglu, combine_check_all_tokens, tile_rows, to_dev, to_np
 from workloads import CONFIGS, make_inputs, make_swiglu_weights_device
 
 pytestmark = pytest.mark.gpu
@@ -50,37 +49,75 @@ def test_grouped_swiglu_does_not_touch_rows_outside_offsets():
     assert (yy[30:] == 7.0).all()
 
 
+def split_tile_rows(offs, n_rows: int, n_col_tiles: int, k_stages: int, n_cus: int):
+    """Host mirror of the grouped kernel's tile plan, for the test only: the
+    row ranges of the tiles of a launch's last, partial round, which the
+    kernel splits along K.  Row tiles are 256 rows from each expert's first
+    row; tiles run in groups of 8 row tiles x all column tiles, row tiles
+    fastest; whole rounds hold n_cus tiles.  Returns [(row0, row_end)] and the
+    number of K parts (1: no split)."""
+    tiles_rows = []
+    offs = np.asarray(offs, np.int64)
+    for e in range(offs.size - 1):
+        for r0 in range(int(offs[e]), int(offs[e + 1]), 256):
+            tiles_rows.append((r0, int(offs[e + 1])))
+    m_real = len(tiles_rows)
+    tiles = m_real * n_col_tiles
+    full = tiles // n_cus * n_cus
+    tail = tiles - full
+    split = 1
+    if tail > 0 and k_stages % 2 == 0:
+        split = max(1, min(n_cus // tail, 8, k_stages // 2))
+    out = set()
+    for t in range(full, tiles):
+        g = t // (8 * n_col_tiles)
+        m0 = g * 8
+        gm = min(8, m_real - m0)
+        i = t - g * 8 * n_col_tiles
+        out.add(tiles_rows[m0 + i % gm])
+    return sorted(out), split
+
+
 def test_mixtral_layer_full_size():
     """Route -> sorted dispatch -> grouped SwiGLU reading the rows in place ->
-    combine, at N=8192, D=4096, E=8, k=2, F=14336; sampled rows checked."""
+    combine, at N=8192, D=4096, E=8, k=2, F=14336.  Checked against the
+    oracle: one row of every 256-row tile of every expert plus each expert's
+    last row (so every tile of both launches, including the K-split tiles of a
+    last partial round), both in h (the gate/up launch's output, read from the
+    workspace) and in y; the combine on every token."""
     cfg = CONFIGS["mixtral"]
     inp = make_inputs(cfg)
     w = make_swiglu_weights_device(cfg)
     idx, tw = moe.moe_route_topk(to_dev(inp["logits"]), cfg.top_k)
     res = moe.moe_dispatch(to_dev(inp["x"]), idx, cfg.n_experts, 1, sort=-1, sort_cutoff=cfg.sort_cutoff)
     assert res.sorted                                    # N = 8192 > cutoff 256
-    y = moe.moe_grouped_swiglu(res.rows, res.expert_offsets, w["w_gate"], w["w_up"], w["w_down"])
+    n_rows, f, d = cfg.n_tokens * cfg.top_k, cfg.ffn, cfg.hidden
+    ws = torch.empty(moe.moe_grouped_swiglu_workspace_bytes(n_rows, cfg.n_experts, d, f),
+                     dtype=torch.uint8, device=DEV)
+    y = moe.moe_grouped_swiglu(res.rows, res.expert_offsets, w["w_gate"], w["w_up"], w["w_down"],
+                               workspace=ws)
     out = moe.moe_combine(y, res.dst_pos, tw)
     torch.cuda.synchronize()
+    h = ws[: n_rows * f * 2].view(torch.bfloat16).view(n_rows, f)     # h [R, F] opens the workspace
     offs = to_np(res.expert_offsets)
-    rng = np.random.default_rng(0)
-    sample = []
-    for ex in range(cfg.n_experts):                      # 3 rows per non-empty expert
-        if offs[ex + 1] > offs[ex]:
-            sample += list(rng.integers(offs[ex], offs[ex + 1], 3))
-    sample = np.array(sorted(set(sample)))
+    sample = tile_rows(offs, 256, np.random.default_rng(0))
+    n_cus = min(256, torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8)
+    split_any = False
+    for n_col_tiles, k_stages in ((f // 128, d // 64), (d // 256, f // 64)):
+        ranges, split = split_tile_rows(offs, n_rows, n_col_tiles, k_stages, n_cus)
+        split_any |= split > 1 and bool(ranges)
+        for r0, r1 in ranges:                           # every last-round tile has a checked row
+            assert np.any((sample >= r0) & (sample < min(r0 + 256, r1))), (r0, r1)
+    assert split_any, "the full-size layer should exercise the K-split last round"
     rows = to_np(res.rows)[sample]
     experts = to_np(res.row_expert)[sample]
     host_w = {k: v.view(torch.int16).cpu().numpy().view(np.uint16) for k, v in w.items()}
+    ref_h = swiglu_hidden(rows, experts, host_w["w_gate"], host_w["w_up"])
+    check_swiglu(to_np(h)[sample], ref_h, experts, what="mixtral h")
     ref = swiglu_rows(rows, experts, host_w["w_gate"], host_w["w_up"], host_w["w_down"])
-    check_swiglu(to_np(y)[sample], ref, experts, what="mixtral")
-    # the combine over the GEMM output, for tokens whose both rows were sampled: check
-    # the combine itself on the GPU's own y (identical inputs)
-    yf = codecs.bf16_bits_to_f32(to_np(y))
-    toks = rng.choice(cfg.n_tokens, 64, replace=False)
-    exact = combine_f64(yf, to_np(res.dst_pos), to_np(tw), cfg.top_k, tokens=toks)
-    mag = combine_f64(np.abs(yf), to_np(res.dst_pos), np.abs(to_np(tw)), cfg.top_k, tokens=toks)
-    check_combine(to_np(out)[toks], exact, mag, True, what="mixtral combine")
+    check_swiglu(to_np(y)[sample], ref, experts, what="mixtral y")
+    # the combine over the GEMM output, every token, on the GPU's own y
+    combine_check_all_tokens(out, y, res.dst_pos, tw, cfg.top_k, True, what="mixtral combine")
 
 
 def test_grouped_swiglu_many_experts():
