@@ -10,8 +10,9 @@ from .api import (DispatchResult, MoeError, moe_abi_version, moe_combine, moe_de
                   moe_gather_swiglu_workspace_bytes,
                   moe_grouped_gemm_fp8, moe_grouped_swiglu,
                   moe_grouped_swiglu_workspace_bytes, moe_resolve_sorted, moe_route_dispatch,
-                  moe_route_dispatch_workspace_bytes, moe_route_topk, moe_scatter_rows)
-from ._lib import LIB_PATH, MOE_SORT_AUTO, MOE_SORT_OFF, MOE_SORT_ON
+                  moe_route_dispatch_noalloc, moe_route_dispatch_workspace_bytes, moe_route_topk,
+                  moe_scatter_rows)
+from ._lib import LIB_PATH, MOE_NOALLOC_SCRATCH_BYTES, MOE_SORT_AUTO, MOE_SORT_OFF, MOE_SORT_ON
 
 __all__ = ["DispatchResult", "MoeError", "moe_abi_version", "moe_combine", "moe_dequant_rows",
            "moe_dispatch", "moe_dispatch_workspace_bytes", "moe_gather_rows",
@@ -19,5 +20,6 @@ __all__ = ["DispatchResult", "MoeError", "moe_abi_version", "moe_combine", "moe_
            "moe_gather_swiglu_workspace_bytes",
            "moe_grouped_gemm_fp8", "moe_grouped_swiglu",
            "moe_grouped_swiglu_workspace_bytes", "moe_resolve_sorted", "moe_route_topk",
-           "moe_scatter_rows", "moe_route_dispatch", "moe_route_dispatch_workspace_bytes",
-           "LIB_PATH", "MOE_SORT_AUTO", "MOE_SORT_OFF", "MOE_SORT_ON"]
+           "moe_scatter_rows", "moe_route_dispatch", "moe_route_dispatch_noalloc",
+           "moe_route_dispatch_workspace_bytes",
+           "LIB_PATH", "MOE_NOALLOC_SCRATCH_BYTES", "MOE_SORT_AUTO", "MOE_SORT_OFF", "MOE_SORT_ON"]

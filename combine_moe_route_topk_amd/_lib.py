@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_dc.s
 MOE_F32, MOE_BF16, MOE_F8E4M3 = 0, 1, 2
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 MOE_SORT_AUTO, MOE_SORT_OFF, MOE_SORT_ON = -1, 0, 1
+MOE_NOALLOC_SCRATCH_BYTES = (1 << 20) + 256      # include/moe_dc.h
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
                 4: "MOE_ERR_HIP"}
 
@@ -36,6 +37,9 @@ SIGNATURES = {
     "moe_route_dispatch": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _i32, _i64, _i64, _i32, _i32, _i32,
                                           _i32, _i32, ctypes.POINTER(_i32), _p, _p, _p, _p, _p, _p,
                                           _p, _p, _p, _sz, _p]),
+    "moe_route_dispatch_noalloc": (ctypes.c_int, [_p, _i32, _p, _p, _p, _p, _i32, _i64, _i64, _i32,
+                                                  _i32, _i32, _i32, _i32, ctypes.POINTER(_i32), _p,
+                                                  _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_scatter_rows": (ctypes.c_int, [_p, _i64, _i64, _i32, _p, _p, _p]),
     "moe_gather_rows": (ctypes.c_int, [_p, _i64, _i64, _i32, _p, _i64, _p, _p]),
     "moe_combine": (ctypes.c_int, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _i32, _p]),

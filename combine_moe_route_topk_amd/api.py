@@ -18,7 +18,7 @@ from ._lib import (MOE_BF16, MOE_F32, MOE_F8E4M3, MOE_SORT_AUTO, MoeError, check
 
 __all__ = ["moe_route_topk", "moe_resolve_sorted", "moe_dispatch_workspace_bytes", "moe_dispatch",
            "moe_combine", "moe_dequant_rows", "moe_scatter_rows", "moe_gather_rows",
-           "moe_route_dispatch", "moe_route_dispatch_workspace_bytes", "moe_grouped_swiglu_workspace_bytes",
+           "moe_route_dispatch", "moe_route_dispatch_noalloc", "moe_route_dispatch_workspace_bytes", "moe_grouped_swiglu_workspace_bytes",
            "moe_grouped_swiglu", "moe_grouped_gemm_fp8", "moe_gather_swiglu_workspace_bytes",
            "moe_gather_swiglu", "moe_gather_swiglu_combine", "moe_abi_version", "DispatchResult",
            "MoeError"]
@@ -196,15 +196,9 @@ def moe_route_dispatch_workspace_bytes(n_tokens: int, n_experts: int, k: int,
     return int(lib.moe_route_dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments))
 
 
-def moe_route_dispatch(logits: torch.Tensor, x: Optional[torch.Tensor], k: int,
-                       n_segments: int = 1, renormalize: bool = True, sort: int = MOE_SORT_AUTO,
-                       sort_cutoff: int = 256, x_scales: Optional[torch.Tensor] = None,
-                       topk_idx: Optional[torch.Tensor] = None,
-                       topk_w: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None,
-                       out: Optional[DispatchResult] = None, want_row_expert: bool = True,
-                       stream=None):
-    """Routing and dispatch in one call -> (topk_idx, topk_w, DispatchResult)."""
+def _route_dispatch_prepare(logits, x, k, n_segments, x_scales, topk_idx, topk_w, out,
+                            want_row_expert):
+    """Shared checks and output allocation of the two route + dispatch calls."""
     _need(logits, "logits", (torch.float32,))
     if logits.dim() != 2:
         raise ValueError("logits must be [N, E]")
@@ -229,6 +223,20 @@ def moe_route_dispatch(logits: torch.Tensor, x: Optional[torch.Tensor], k: int,
                              torch.empty(nk, **i32),
                              torch.empty(nk, **i32) if want_row_expert else None, rows, rs)
     _check_dispatch_out(out, n, k, e, n_segments, x, x_scales, dev)
+    return dev, n, e, dtype, hidden, topk_idx, topk_w, out
+
+
+def moe_route_dispatch(logits: torch.Tensor, x: Optional[torch.Tensor], k: int,
+                       n_segments: int = 1, renormalize: bool = True, sort: int = MOE_SORT_AUTO,
+                       sort_cutoff: int = 256, x_scales: Optional[torch.Tensor] = None,
+                       topk_idx: Optional[torch.Tensor] = None,
+                       topk_w: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       out: Optional[DispatchResult] = None, want_row_expert: bool = True,
+                       stream=None):
+    """Routing and dispatch in one call -> (topk_idx, topk_w, DispatchResult)."""
+    dev, n, e, dtype, hidden, topk_idx, topk_w, out = _route_dispatch_prepare(
+        logits, x, k, n_segments, x_scales, topk_idx, topk_w, out, want_row_expert)
     if workspace is None:
         wsb = moe_route_dispatch_workspace_bytes(n, e, k, n_segments)
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
@@ -240,6 +248,31 @@ def moe_route_dispatch(logits: torch.Tensor, x: Optional[torch.Tensor], k: int,
         _ptr(out.row_scales), _ptr(out.expert_counts), _ptr(out.expert_offsets),
         _ptr(out.segment_offsets), _ptr(out.src_pair), _ptr(out.dst_pos), _ptr(out.row_expert),
         _ptr(workspace), workspace.numel(), _stream(stream)))
+    out.sorted = bool(used.value)
+    return topk_idx, topk_w, out
+
+
+def moe_route_dispatch_noalloc(logits: torch.Tensor, x: Optional[torch.Tensor], k: int,
+                               n_segments: int = 1, renormalize: bool = True,
+                               sort: int = MOE_SORT_AUTO, sort_cutoff: int = 256,
+                               x_scales: Optional[torch.Tensor] = None,
+                               topk_idx: Optional[torch.Tensor] = None,
+                               topk_w: Optional[torch.Tensor] = None,
+                               out: Optional[DispatchResult] = None,
+                               want_row_expert: bool = True, stream=None):
+    """moe_route_dispatch without a workspace: the library's static per-GPU
+    scratch array serves instead, and the C call allocates nothing.  A caller
+    that cannot allocate passes every output (topk_idx, topk_w, out); calls
+    that overlap on one GPU race on the shared scratch."""
+    dev, n, e, dtype, hidden, topk_idx, topk_w, out = _route_dispatch_prepare(
+        logits, x, k, n_segments, x_scales, topk_idx, topk_w, out, want_row_expert)
+    used = ctypes.c_int32(-1)
+    check("moe_route_dispatch_noalloc", lib.moe_route_dispatch_noalloc(
+        _ptr(logits), int(bool(renormalize)), _ptr(topk_idx), _ptr(topk_w), _ptr(x), _ptr(x_scales),
+        dtype, n, hidden, e, k, n_segments, sort, sort_cutoff, ctypes.byref(used), _ptr(out.rows),
+        _ptr(out.row_scales), _ptr(out.expert_counts), _ptr(out.expert_offsets),
+        _ptr(out.segment_offsets), _ptr(out.src_pair), _ptr(out.dst_pos), _ptr(out.row_expert),
+        _stream(stream)))
     out.sorted = bool(used.value)
     return topk_idx, topk_w, out
 

@@ -226,6 +226,54 @@ size_t moe_route_dispatch_workspace_bytes(int64_t n_tokens, int32_t n_experts, i
   return moe::route_dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments);
 }
 
+}  // extern "C"
+
+namespace {
+
+// moe_route_dispatch and its allocation-free variant: the same checks and
+// launches; `workspace` is the caller's buffer or the static scratch.
+int route_dispatch_impl(const char* fn, const float* logits, int32_t renormalize,
+                        int32_t* topk_idx, float* topk_w, const void* x, const float* x_scales,
+                        int32_t dtype, int64_t n_tokens, int64_t hidden, int32_t n_experts,
+                        int32_t k, int32_t n_segments, int32_t sort, int32_t sort_cutoff,
+                        int32_t* sorted_used, void* rows, float* row_scales,
+                        int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* segment_offsets, int32_t* src_pair, int32_t* dst_pos,
+                        int32_t* row_expert, void* workspace, size_t workspace_bytes,
+                        void* stream, bool static_scratch) {
+  const int early = check_routing_sizes(fn, n_tokens, n_experts, k);
+  if (early) return early;
+  if (n_tokens > 0 && (!logits || !topk_idx || !topk_w))
+    return fail(MOE_ERR_ARG, "%s: null routing pointer", fn);
+  const size_t need = moe::route_dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments > 0 ? n_segments : 1);
+  if (static_scratch && need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: these sizes need %zu bytes of scratch, more than the %zu-byte static array "
+                "(use moe_route_dispatch with a workspace)",
+                fn, need, size_t(MOE_NOALLOC_SCRATCH_BYTES));
+  // every argument is checked before the scratch is looked up, so a rejected
+  // call touches no device state (a placeholder address stands in for it)
+  moe::DispatchArgs a;
+  int rc = prepare_dispatch(fn, x, x_scales, dtype, n_tokens, hidden, topk_idx, n_experts, k,
+                            n_segments, sort, sort_cutoff, rows, row_scales, expert_counts,
+                            expert_offsets, segment_offsets, src_pair, dst_pos, row_expert,
+                            static_scratch ? reinterpret_cast<void*>(uintptr_t(256)) : workspace,
+                            static_scratch ? size_t(MOE_NOALLOC_SCRATCH_BYTES) : workspace_bytes,
+                            need, a);
+  if (rc) return rc;
+  if (static_scratch) {
+    const hipError_t e = moe::noalloc_scratch(static_cast<hipStream_t>(stream), &a.workspace);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  if (sorted_used) *sorted_used = a.sorted;
+  moe::RouteArgs r{logits, renormalize ? 1 : 0, topk_w};
+  return hip_status(moe::launch_route_dispatch(r, a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
 int moe_route_dispatch(const float* logits, int32_t renormalize, int32_t* topk_idx, float* topk_w,
                        const void* x, const float* x_scales, int32_t dtype, int64_t n_tokens,
                        int64_t hidden, int32_t n_experts, int32_t k, int32_t n_segments,
@@ -234,21 +282,26 @@ int moe_route_dispatch(const float* logits, int32_t renormalize, int32_t* topk_i
                        int32_t* segment_offsets, int32_t* src_pair, int32_t* dst_pos,
                        int32_t* row_expert, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  const char* fn = "moe_route_dispatch";
-  const int early = check_routing_sizes(fn, n_tokens, n_experts, k);
-  if (early) return early;
-  if (n_tokens > 0 && (!logits || !topk_idx || !topk_w))
-    return fail(MOE_ERR_ARG, "%s: null routing pointer", fn);
-  const size_t need = moe::route_dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments > 0 ? n_segments : 1);
-  moe::DispatchArgs a;
-  int rc = prepare_dispatch(fn, x, x_scales, dtype, n_tokens, hidden, topk_idx, n_experts, k,
-                            n_segments, sort, sort_cutoff, rows, row_scales, expert_counts,
-                            expert_offsets, segment_offsets, src_pair, dst_pos, row_expert,
-                            workspace, workspace_bytes, need, a);
-  if (rc) return rc;
-  if (sorted_used) *sorted_used = a.sorted;
-  moe::RouteArgs r{logits, renormalize ? 1 : 0, topk_w};
-  return hip_status(moe::launch_route_dispatch(r, a, static_cast<hipStream_t>(stream)), fn);
+  return route_dispatch_impl("moe_route_dispatch", logits, renormalize, topk_idx, topk_w, x,
+                             x_scales, dtype, n_tokens, hidden, n_experts, k, n_segments, sort,
+                             sort_cutoff, sorted_used, rows, row_scales, expert_counts,
+                             expert_offsets, segment_offsets, src_pair, dst_pos, row_expert,
+                             workspace, workspace_bytes, stream, false);
+}
+
+int moe_route_dispatch_noalloc(const float* logits, int32_t renormalize, int32_t* topk_idx,
+                               float* topk_w, const void* x, const float* x_scales, int32_t dtype,
+                               int64_t n_tokens, int64_t hidden, int32_t n_experts, int32_t k,
+                               int32_t n_segments, int32_t sort, int32_t sort_cutoff,
+                               int32_t* sorted_used, void* rows, float* row_scales,
+                               int32_t* expert_counts, int32_t* expert_offsets,
+                               int32_t* segment_offsets, int32_t* src_pair, int32_t* dst_pos,
+                               int32_t* row_expert, void* stream) {
+  return route_dispatch_impl("moe_route_dispatch_noalloc", logits, renormalize, topk_idx, topk_w,
+                             x, x_scales, dtype, n_tokens, hidden, n_experts, k, n_segments, sort,
+                             sort_cutoff, sorted_used, rows, row_scales, expert_counts,
+                             expert_offsets, segment_offsets, src_pair, dst_pos, row_expert,
+                             nullptr, 0, stream, true);
 }
 
 int moe_scatter_rows(const void* x, int64_t n_tokens, int64_t row_bytes, int32_t k,

@@ -25,6 +25,8 @@
 // Small problems (NK <= 4096, at most 256 buckets) run count, scan and rank
 // in one workgroup.  Nothing is read back to the host: NK rows is always the
 // output size.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -646,6 +648,48 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
 
 size_t route_dispatch_workspace_bytes(int64_t n_tokens, int n_experts, int k, int n_segments) {
   return dispatch_workspace_bytes(n_tokens, n_experts, k, n_segments);
+}
+
+// ------------------------------------------------------------------ allocation-free scratch
+// The workspace of moe_route_dispatch_noalloc: one copy of this array per GPU,
+// alive until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host it names a stand-in, not the device copy): the device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+namespace {
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
+  *ptr = nullptr;
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream) {                      // the kernels run on the stream's device
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return e;
+    dev = int(sd);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_route_dispatch(const RouteArgs& r, const DispatchArgs& a, hipStream_t stream) {

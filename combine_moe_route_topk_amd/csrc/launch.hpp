@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/moe_dc.h"
+
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
@@ -63,6 +65,12 @@ hipError_t launch_route_copy_identity(const float* logits, int64_t n_tokens, int
                                       hipStream_t stream);
 size_t route_dispatch_workspace_bytes(int64_t n_tokens, int n_experts, int k, int n_segments);
 hipError_t launch_route_dispatch(const RouteArgs& r, const DispatchArgs& a, hipStream_t stream);
+
+// Allocation-free variant: the device address of a static per-GPU scratch
+// array of kNoAllocScratchBytes (256-byte aligned) on the stream's device,
+// looked up on the first call on that device and kept.
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 
 // Row copies on their own (byte payloads): scatter form rows[dst_pos[q]] =
 // x[q / k] and gather form rows[p] = x[src_pair[p] / k].

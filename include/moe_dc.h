@@ -203,6 +203,35 @@ int moe_route_dispatch(const float* logits, int32_t renormalize, int32_t* topk_i
                        int32_t* row_expert, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* Bytes of the static per-GPU scratch array of moe_route_dispatch_noalloc. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)1048576 + 256)
+
+/* moe_route_dispatch_noalloc -- moe_route_dispatch for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and outputs (bit for bit)
+ * without the workspace: its scratch is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until the
+ * process ends; the array's device address is looked up on the first call on
+ * a device (the device of `stream`, or the current one for the null stream)
+ * and kept.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine) and needs no zeroed memory: every scratch byte it reads was
+ * written earlier in the same call.  All calls on one GPU share the array, so
+ * calls that overlap on one GPU (other streams, other host threads) race:
+ * serialise them.
+ * Errors: those of moe_route_dispatch; MOE_ERR_UNSUPPORTED when
+ * moe_route_dispatch_workspace_bytes(N, E, k, G) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (E <= 256 always fits; E = 1024 fits up to
+ * N*k = 262144 pairs), checked before any device call; MOE_ERR_HIP if the
+ * scratch address cannot be obtained. */
+int moe_route_dispatch_noalloc(const float* logits, int32_t renormalize, int32_t* topk_idx,
+                               float* topk_w, const void* x, const float* x_scales, int32_t dtype,
+                               int64_t n_tokens, int64_t hidden, int32_t n_experts, int32_t k,
+                               int32_t n_segments, int32_t sort, int32_t sort_cutoff,
+                               int32_t* sorted_used, void* rows, float* row_scales,
+                               int32_t* expert_counts, int32_t* expert_offsets,
+                               int32_t* segment_offsets, int32_t* src_pair, int32_t* dst_pos,
+                               int32_t* row_expert, void* stream);
+
 /* moe_scatter_rows -- the row copy of moe_dispatch on its own, scatter form
  * (packet_scatter / dispatch_local of [MLX-EP]):
  *   rows[dst_pos[t*k + j]] = x[t]   for every token t and slot j,

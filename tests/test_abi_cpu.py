@@ -257,3 +257,36 @@ def test_gather_swiglu_combine_errors():
     assert g(*args(rows=ctypes.c_void_p(0x1008))) == UNSUP
     assert g(*args(wsb=need - 1)) == WS and g(*args(ws=ctypes.c_void_p(0x1040))) == WS
     assert g(*args(n_rows=0, rows=None, tw=None, out=None, ws=None, wsb=0)) == 0
+
+
+def test_route_dispatch_noalloc_errors_before_any_device_call():
+    """The allocation-free variant checks every argument, and that its sizes
+    fit the static scratch, before it looks the scratch up (no GPU here: a
+    call that got that far would report MOE_ERR_HIP instead)."""
+    f = lib.moe_route_dispatch_noalloc
+
+    def call(**kw):
+        a = dict(logits=FAKE, renorm=1, idx=FAKE, w=FAKE, x=FAKE, xs=None, dtype=1, n=4, d=64, e=8,
+                 k=2, g=1, sort=1, cutoff=256, used=None, rows=FAKE, rs=None, counts=FAKE, offs=FAKE,
+                 segs=FAKE, src=FAKE, dst=FAKE, rexp=FAKE)
+        a.update(kw)
+        return f(a["logits"], a["renorm"], a["idx"], a["w"], a["x"], a["xs"], a["dtype"], a["n"],
+                 a["d"], a["e"], a["k"], a["g"], a["sort"], a["cutoff"], a["used"], a["rows"], a["rs"],
+                 a["counts"], a["offs"], a["segs"], a["src"], a["dst"], a["rexp"], None)
+
+    assert call(logits=None) == ARG
+    assert call(k=9) == ARG
+    assert call(g=3) == ARG
+    assert call(rows=None) == ARG
+    assert call(e=2048) == UNSUP
+    # E = 1024 with 2^19 pairs needs 512 chunk histograms of 4 KB: more than the array
+    need = lib.moe_route_dispatch_workspace_bytes(1 << 16, 1024, 8, 1)
+    assert need > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(n=1 << 16, e=1024, k=8) == UNSUP
+    assert b"static array" in lib.moe_last_error()
+    # the binding's constant is the header's
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) \+ (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) + int(m.group(2)) == _lib.MOE_NOALLOC_SCRATCH_BYTES
+    # the largest sizes at E <= 256 fit
+    for n, e, k in ((1 << 18, 256, 8), (4096, 256, 8), (32768, 1024, 8), (1 << 20, 64, 2)):
+        assert lib.moe_route_dispatch_workspace_bytes(n, e, k, 1) <= _lib.MOE_NOALLOC_SCRATCH_BYTES
