@@ -59,6 +59,12 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a plain device copy of known size (PMC counter calibration)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="run only torch's bf16 linear (hipBLASLt) on the Mixtral-like layer's "
+                         "dense and per-expert products, for comparison with the grouped SwiGLU")
+    ap.add_argument("--crossover", action="store_true",
+                    help="run only the sorted/unsorted crossover table of the decode layer "
+                         "with SwiGLU experts over a range of token counts")
     return ap.parse_args()
 
 
@@ -155,15 +161,17 @@ def capture(torch, step, n):
     return g
 
 
-def graph_times(torch, step, steps, warmup):
+def graph_times(torch, step, steps, warmup, replays=11):
     """Per-step wall time of the step in HIP graphs, in ms.
 
     Timed steps: K consecutive steps captured as one graph, the way a serving
-    loop captures a whole forward pass of K layers, replayed once between two
-    synchronizations.  Untimed before it: W replays of a one-step graph, then
-    one replay of the K-step graph (its one-time upload to the device).  The
-    one-step graph is also timed over K replays: that figure includes the
-    launch of a graph per step.  Returns (K-step graph, one-step graph)."""
+    loop captures a whole forward pass of K layers, replayed `replays` times,
+    each replay between two synchronizations on the wall clock.  Untimed
+    before it: W replays of a one-step graph, then one replay of the K-step
+    graph (its one-time upload to the device).  The one-step graph is also
+    timed over K replays: that figure includes the launch of a graph per step.
+    Returns ({p10, p50, p90} of the K-step graph's per-step time over the
+    replays, one-step graph)."""
     g1 = capture(torch, step, 1)
     for _ in range(warmup):
         g1.replay()
@@ -176,10 +184,43 @@ def graph_times(torch, step, steps, warmup):
     gk = capture(torch, step, steps)
     gk.replay()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    gk.replay()
+    per_step = []
+    for _ in range(replays):
+        t0 = time.perf_counter()
+        gk.replay()
+        torch.cuda.synchronize()
+        per_step.append((time.perf_counter() - t0) / steps * 1e3)
+    del gk, g1
+    return pct(per_step), one
+
+
+def pct(values):
+    """{p10, p50, p90} of a list of timings."""
+    v = np.asarray(values, dtype=np.float64)
+    return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
+            "p90": float(np.percentile(v, 90)), "n": int(v.size)}
+
+
+def cold_times(torch, step, reps=21, flush_bytes=1 << 30):
+    """Per-step time with cold caches, in ms: before every timed step, untimed,
+    an elementwise pass reads and writes a 1 GiB buffer (4x the 256 MB
+    last-level cache), so the step's inputs come from HBM.  Each step is a
+    one-step graph replay timed with HIP events on the launch stream (the
+    flush is queued ahead of them, so no launch gap is timed)."""
+    flush = torch.zeros(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
+    g1 = capture(torch, step, 1)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        flush.add_(1.0)
+        e0.record(stream)
+        g1.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e3, one
+    out = pct([e0.elapsed_time(e1) for e0, e1 in evs])
+    del flush, g1
+    return out
 
 
 def check_outputs(path):
@@ -204,6 +245,13 @@ def check_outputs(path):
     got = path.out[torch.from_numpy(toks).to(path.out.device)].float().cpu().numpy()
     if not np.all(np.abs(got - exact) <= 2.0 ** -7 * np.abs(exact) + 1e-30):
         raise RuntimeError("combine output of the timed run differs from the oracle")
+
+
+def expert_load(res):
+    """Realised rows per expert of a dispatch: the histogram's extremes."""
+    c = res.expert_counts.cpu().numpy()
+    return {"max": int(c.max()), "min": int(c.min()), "mean": round(float(c.mean()), 2),
+            "empty_experts": int((c == 0).sum()), "top4": sorted(c.tolist())[-4:][::-1]}
 
 
 def dc_bytes(cfg):
@@ -258,10 +306,13 @@ def time_all_configs(torch, moe, steps, warmup):
 
         reps = max(steps, 50)
         ms_k, ms_1 = graph_times(torch, step, reps, warmup)
-        us = ms_k * 1e3 / len(sorts)
+        us = ms_k["p50"] * 1e3 / len(sorts)
         us1 = ms_1 * 1e3 / len(sorts)
         b = dc_bytes(cfg)["total"]
-        out[name] = {"us_per_layer": round(us, 2), "us_per_layer_graph1": round(us1, 2),
+        out[name] = {"us_per_layer": round(us, 2),
+                     "us_per_layer_p10_p90": [round(ms_k["p10"] * 1e3 / len(sorts), 2),
+                                              round(ms_k["p90"] * 1e3 / len(sorts), 2)],
+                     "us_per_layer_graph1": round(us1, 2),
                      "GB_per_s": round(b / (us * 1e-6) / 1e9, 1),
                      "frac_of_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "bytes": b, "mode": "alternating unsorted/sorted" if len(sorts) > 1 else
@@ -561,6 +612,116 @@ def calib_copy(torch):
     print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
 
 
+def library_gemm(torch, reps=10):
+    """torch's bf16 linear (hipBLASLt on ROCm) on the products of the
+    Mixtral-like layer (16384 rows, D=4096, F=14336, 8 experts of ~2048 rows):
+    the gate and up projections as one dense [16384, 4096] x [4096, 28672]
+    product and the down projection as [16384, 14336] x [14336, 4096], and the
+    same per expert (2048 rows).  Activations N(0, 1), weights N(0, 0.02), as
+    in the workload (the matrix cores' power depends on the data)."""
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    stream = torch.cuda.current_stream()
+    rec = {}
+    for name, m, n, k in (("dense_gate_up", 16384, 28672, 4096), ("dense_down", 16384, 4096, 14336),
+                          ("expert_gate_up", 2048, 28672, 4096), ("expert_down", 2048, 4096, 14336)):
+        a = torch.randn((m, k), device=dev, generator=gen).to(torch.bfloat16)
+        w = (torch.randn((n, k), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+        for _ in range(3):
+            out = torch.nn.functional.linear(a, w)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            out = torch.nn.functional.linear(a, w)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        rec[name] = {"m": m, "n": n, "k": k, "ms": round(ms, 4),
+                     "tflops": round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 1)}
+        del a, w, out
+    layer = rec["dense_gate_up"]["ms"] + rec["dense_down"]["ms"]
+    per_expert = 8 * (rec["expert_gate_up"]["ms"] + rec["expert_down"]["ms"])
+    flop = 2.0 * 16384 * 4096 * 14336 * 3
+    rec["layer_dense_ms"] = round(layer, 3)
+    rec["layer_dense_tflops"] = round(flop / (layer * 1e-3) / 1e12, 1)
+    rec["layer_8_expert_calls_ms"] = round(per_expert, 3)
+    rec["layer_8_expert_calls_tflops"] = round(flop / (per_expert * 1e-3) / 1e12, 1)
+    print(json.dumps({"library_gemm": rec, "what": "torch.nn.functional.linear bf16 (hipBLASLt), "
+                      "HIP events over 10 calls after 3 warm-up calls"}), flush=True)
+
+
+def crossover(torch, moe, steps=5, warmup=2):
+    """The sorted/unsorted switch measured on MoE layers with SwiGLU experts
+    over a range of token counts: each layer is route + dispatch + expert FFN
+    + combine, K steps in one graph.
+      unsorted+gather: identity layout, per-row-expert FFN (moe_gather_swiglu)
+      sorted+grouped:  expert-major layout, grouped FFN (moe_grouped_swiglu)
+      sorted+gather:   expert-major layout, per-row-expert FFN
+    and with identity experts (route + dispatch + combine) in both modes.
+    Two expert shapes: the decode workload's (D=7168, E=256, top-8, F=2048)
+    and the Mixtral-like one (D=4096, E=8, top-2, F=14336)."""
+    from workloads import CONFIGS, DECODE_FFN, make_inputs, make_swiglu_weights_device
+    dev = torch.device("cuda:0")
+    result = {}
+    for base, ns in ((DECODE_FFN, (16, 32, 64, 128, 256, 512, 640, 768, 896, 1024, 2048)),
+                     (CONFIGS["mixtral"], (8, 16, 32, 64, 128, 256, 512))):
+        w = make_swiglu_weights_device(base)
+        e, d, f, k = base.n_experts, base.hidden, base.ffn, base.top_k
+        table = []
+        for n in ns:
+            cfg = base.with_tokens(n)
+            inp = make_inputs(cfg)
+            logits = torch.from_numpy(inp["logits"]).to(dev)
+            x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+            rd_ws = torch.empty(moe.moe_route_dispatch_workspace_bytes(n, e, k, 1),
+                                dtype=torch.uint8, device=dev)
+            gws = torch.empty(moe.moe_gather_swiglu_workspace_bytes(n * k, e, d, f),
+                              dtype=torch.uint8, device=dev)
+            sws = torch.empty(moe.moe_grouped_swiglu_workspace_bytes(n * k, e, d, f),
+                              dtype=torch.uint8, device=dev)
+            y = torch.empty((n * k, d), dtype=torch.bfloat16, device=dev)
+            out = torch.empty((n, d), dtype=torch.bfloat16, device=dev)
+            row = {"n_tokens": n, "rows_per_expert": round(n * k / e, 2)}
+            for mode in ("unsorted+gather", "sorted+grouped", "sorted+gather",
+                         "identity unsorted", "identity sorted"):
+                sort = 0 if mode in ("unsorted+gather", "identity unsorted") else 1
+                idx, tw, res = moe.moe_route_dispatch(logits, x, k, 1, True, sort, 256,
+                                                      workspace=rd_ws)
+
+                def step(sort=sort, mode=mode, idx=idx, tw=tw, res=res):
+                    moe.moe_route_dispatch(logits, x, k, 1, True, sort, 256, topk_idx=idx,
+                                           topk_w=tw, workspace=rd_ws, out=res)
+                    if mode.endswith("gather"):
+                        moe.moe_gather_swiglu(res.rows, res.row_expert, w["w_gate"], w["w_up"],
+                                              w["w_down"], y=y, workspace=gws)
+                        moe.moe_combine(y, res.dst_pos, tw, out=out)
+                    elif mode.endswith("grouped"):
+                        moe.moe_grouped_swiglu(res.rows, res.expert_offsets, w["w_gate"],
+                                               w["w_up"], w["w_down"], y=y, workspace=sws)
+                        moe.moe_combine(y, res.dst_pos, tw, out=out)
+                    else:
+                        moe.moe_combine(res.rows, res.dst_pos, tw, out=out)
+
+                gk, _ = graph_times(torch, step, steps if "identity" not in mode else 50, warmup,
+                                    replays=5)
+                row[mode] = round(gk["p50"] * 1e3, 2)
+                del res, idx, tw
+            table.append(row)
+            print(json.dumps({base.name: row}), flush=True)
+            del logits, x, rd_ws, gws, sws, y, out
+        del w
+        torch.cuda.empty_cache()
+        cross = [r["n_tokens"] for r in table if r["sorted+grouped"] < r["unsorted+gather"]]
+        result[base.name] = {"table": table,
+                             "first_n_where_sorted_grouped_wins": cross[0] if cross else None,
+                             "shape": f"D={base.hidden}, E={base.n_experts}, top-{base.top_k}, "
+                                      f"F={base.ffn}"}
+    print(json.dumps({"crossover": result, "unit": "us per layer (median of 5 replays of a "
+                      "K-step graph)"}), flush=True)
+
+
 def copy_ceiling(torch, nbytes, reps=10):
     """A plain device copy moving the same bytes as one step (half read, half
     written), timed with HIP events: the copy ceiling the path is compared with."""
@@ -594,24 +755,34 @@ def main():
     if args.calib_copy:
         calib_copy(torch)
         return
+    if args.library_gemm:
+        library_gemm(torch)
+        return
     import combine_moe_route_topk_amd as moe
+    if args.crossover:
+        crossover(torch, moe)
+        return
     from workloads import CONFIGS
 
     cfg = CONFIGS[args.workload]
-    path = Path(cfg, torch, moe)
+    path = Path(cfg, torch, moe, split=False)
     ms_eager, stage_mean_us, stage_med_us = time_path(path, args.steps, args.warmup)
     check_outputs(path)
-    ms, ms_g1 = graph_times(torch, path.step, args.steps, args.warmup)   # the timed steps
+    gk, ms_g1 = graph_times(torch, path.step, args.steps, args.warmup)   # the timed steps
+    ms = gk["p50"]
+    check_outputs(path)
+    cold = cold_times(torch, path.step)
     check_outputs(path)
     n, d, e, k, g = cfg.n_tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.n_segments
     b = algorithmic_bytes(n, d, e, k, g, cfg.elem_bytes)
     value = b["total"] / (ms * 1e-3) / 1e9
     ceiling = copy_ceiling(torch, b["total"])
 
-    names = ["route+maps", "scatter", "combine"]
-    dom = "scatter" if stage_mean_us[1] >= stage_mean_us[2] else "combine"
-    di = names.index(dom)
-    achieved = b[dom] / (stage_mean_us[di] * 1e-6) / 1e9
+    # one call routes and dispatches (maps and rows); the combine is the other
+    stages = {"route+dispatch": float(stage_mean_us[0] + stage_mean_us[1]),
+              "combine": float(stage_mean_us[2])}
+    dom = "combine"
+    achieved = b[dom] / (stages[dom] * 1e-6) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
@@ -621,7 +792,7 @@ def main():
             traffic = ent["hbm_bytes_per_launch"]
     roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                     unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    algorithmic_bytes=b[dom], avg_us=round(float(stage_mean_us[di]), 2))
+                    algorithmic_bytes=b[dom], avg_us=round(stages[dom], 2))
 
     rec = {
         "metric": "dispatch+combine µs/layer and HBM GB/s (% peak) at 128 and 4096 tokens",
@@ -639,17 +810,22 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.note}", "n_tokens": n, "hidden": d,
                    "n_experts": e, "top_k": k, "n_segments": g,
                    "sort": "sorted" if path.res.sorted else "unsorted", "experts": "identity",
-                   "bytes_per_step": b["total"]},
+                   "bytes_per_step": b["total"], "expert_load": expert_load(path.res)},
         "timing": "K consecutive steps captured as one HIP graph (a K-layer forward pass), "
-                  "replayed once, wall clock between synchronizations; graph1 = K replays "
-                  "of a one-step graph; stages from HIP events over K eager steps",
+                  "replayed 11 times, wall clock between synchronizations around each replay; "
+                  "value and ms_per_step from the median replay; graph1 = K replays of a "
+                  "one-step graph; cold = one-step graph after a 1 GiB read+write flush, HIP "
+                  "events; stages from HIP events over K eager steps",
         "us_per_layer": round(ms * 1e3, 2),
+        "us_per_layer_pct": {q: round(v * 1e3, 2) for q, v in gk.items() if q != "n"},
+        "us_per_layer_cold": {q: round(v * 1e3, 2) for q, v in cold.items() if q != "n"},
         "us_per_layer_graph1": round(ms_g1 * 1e3, 2),
         "us_per_layer_eager": round(ms_eager * 1e3, 2),
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "copy_ceiling": ceiling,
         "frac_of_copy_ceiling": round(value / ceiling["GB_per_s"], 4),
-        "stages_us": {nm: round(float(v), 2) for nm, v in zip(names, stage_mean_us)},
+        "stages_us": {nm: round(v, 2) for nm, v in stages.items()},
+        "calls": "moe_route_dispatch (routing, maps and rows) + moe_combine",
         "roofline": roofline,
     }
     if not args.no_decode and args.workload == "prefill":
@@ -659,14 +835,21 @@ def main():
         check_outputs(dpath)
         db = algorithmic_bytes(dcfg.n_tokens, dcfg.hidden, dcfg.n_experts, dcfg.top_k,
                                dcfg.n_segments, dcfg.elem_bytes)
-        gms, gms1 = graph_times(torch, dpath.step, max(args.steps, 200), args.warmup)
+        dk, gms1 = graph_times(torch, dpath.step, max(args.steps, 200), args.warmup)
+        gms = dk["p50"]
+        check_outputs(dpath)
+        dcold = cold_times(torch, dpath.step)
         check_outputs(dpath)
         rec["decode"] = {"workload": f"decode: {dcfg.note}", "us_per_layer": round(gms * 1e3, 2),
+                         "us_per_layer_pct": {q: round(v * 1e3, 2) for q, v in dk.items() if q != "n"},
+                         "us_per_layer_cold": {q: round(v * 1e3, 2) for q, v in dcold.items() if q != "n"},
                          "us_per_layer_graph1": round(gms1 * 1e3, 2),
                          "us_per_layer_eager": round(dms * 1e3, 2),
                          "calls": "moe_route_dispatch (with rows) + moe_combine",
                          "GB_per_s": round(db["total"] / (gms * 1e-3) / 1e9, 1),
-                         "cache": "hot (33 MB of buffers stay in the 256 MB last-level cache)",
+                         "cache": "us_per_layer: hot (the step's 33 MB of buffers can stay in the "
+                                  "256 MB last-level cache between steps); us_per_layer_cold: "
+                                  "1 GiB flush before every step",
                          "stages_us": {"route+dispatch": round(float(dst_us[0] + dst_us[1]), 2),
                                        "combine": round(float(dst_us[2]), 2)}}
     if not args.no_all and args.workload == "prefill":

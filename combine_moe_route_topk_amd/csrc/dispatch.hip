@@ -173,35 +173,87 @@ __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t* __restrict
   for (int i = threadIdx.x; i < n_experts; i += kBlock) out[i] = h[i];
 }
 
+// ------------------------------------------------------------------ row loads
+// Token rows are read once per dispatch: non-temporal loads for the 16-byte
+// path, plain loads for the narrow fallback types.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_once(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <typename V>
+__device__ __forceinline__ V load_once(const V* p) { return *p; }
+
+// An empty asm statement that reads and writes the value's registers: the
+// compiler must have the value in registers (its load waited for) at this point.
+__device__ __forceinline__ void consume(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+__device__ __forceinline__ void consume(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
+__device__ __forceinline__ void consume(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void consume(uint16_t& v) {
+  uint32_t t = v;
+  asm volatile("" : "+v"(t));
+  v = uint16_t(t);
+}
+__device__ __forceinline__ void consume(uint8_t& v) {
+  uint32_t t = v;
+  asm volatile("" : "+v"(t));
+  v = uint8_t(t);
+}
+
 // ------------------------------------------------------------------ rank
-// Block p owns chunk p.  From the [P, E] chunk histograms (L2-resident) it
+// Rank of one chunk.  From the [P, E] chunk histograms (L2-resident) it
 // derives every expert's total and the count in chunks before its own, scans
-// the totals into expert offsets (block 0 also writes counts and offsets),
+// the totals into expert offsets (chunk 0 also writes counts and offsets),
 // forms its per-bucket starting positions, recounts per wave and walks its
 // pairs in order.
-__global__ __launch_bounds__(kBlock) void rank_kernel(const int32_t* __restrict__ idx, int64_t nk,
-                                                      int n_experts, int n_segments, int chunk,
-                                                      int n_chunks, int sorted, int identity,
-                                                      int nbits,
-                                                      const int32_t* __restrict__ hist,
-                                                      int32_t* __restrict__ counts,
-                                                      int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ seg_offsets,
-                                                      int32_t* __restrict__ dst_pos,
-                                                      int32_t* __restrict__ src_pair,
-                                                      int32_t* __restrict__ row_expert) {
+struct RankArgs {
+  const int32_t* idx;
+  int64_t nk;
+  int n_experts, n_segments, chunk, n_chunks, sorted, identity, nbits;
+  const int32_t* hist;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* seg_offsets;
+  int32_t* dst_pos;
+  int32_t* src_pair;
+  int32_t* row_expert;
+};
+
+// LDS of the rank part, carved from dynamic shared memory sized by E and the
+// bucket count (7 KB at E = 256, 28 KB at E = 1024).
+struct RankLds {
+  int* tot;     // [E]
+  int* bef;     // [E]
+  int* off;     // [E + 1]
+  int* wh;      // [waves * buckets]
+  int* wave;    // [waves + 1]
+};
+
+__host__ __device__ constexpr size_t rank_lds_ints(int n_experts, int n_buckets) {
+  return size_t(3) * n_experts + 1 + size_t(kBlock / kWave) * n_buckets + (kBlock / kWave + 1);
+}
+
+__device__ __forceinline__ RankLds rank_lds(int* base, int n_experts, int n_buckets) {
+  RankLds L;
+  L.tot = base;
+  L.bef = L.tot + n_experts;
+  L.off = L.bef + n_experts;
+  L.wh = L.off + n_experts + 1;
+  L.wave = L.wh + (kBlock / kWave) * n_buckets;
+  return L;
+}
+
+__device__ __forceinline__ void rank_chunk(const RankArgs& r, int me, const RankLds& L) {
   constexpr int kWaves = kBlock / kWave;
   constexpr int kPer = kMaxExperts / kBlock;           // experts per thread in the scan
-  __shared__ int s_tot[kMaxExperts];
-  __shared__ int s_bef[kMaxExperts];
-  __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int wh[kWaves * kMaxExperts];
-  __shared__ int s_wave[kWaves + 1];
   const int tid = threadIdx.x;
   const int w = tid / kWave;
-  const int me = blockIdx.x;
-  const int per = n_experts / n_segments;
-  const int n_buckets = sorted ? n_experts : n_segments;
+  const int n_experts = r.n_experts, n_chunks = r.n_chunks;
+  const int32_t* __restrict__ hist = r.hist;
+  const int per = n_experts / r.n_segments;
+  const int n_buckets = r.sorted ? n_experts : r.n_segments;
 
   // 1. totals and before-counts per expert
   for (int e = tid; e < n_experts; e += kBlock) {
@@ -232,10 +284,10 @@ __global__ __launch_bounds__(kBlock) void rank_kernel(const int32_t* __restrict_
       tot += v;
       bef += (c < me) ? v : 0;
     }
-    s_tot[e] = tot;
-    s_bef[e] = bef;
+    L.tot[e] = tot;
+    L.bef[e] = bef;
   }
-  for (int i = tid; i < kWaves * n_buckets; i += kBlock) wh[i] = 0;
+  for (int i = tid; i < kWaves * n_buckets; i += kBlock) L.wh[i] = 0;
   __syncthreads();
 
   // 2. exclusive scan of the totals: thread i takes experts [i*kPer, i*kPer + kPer)
@@ -244,60 +296,67 @@ __global__ __launch_bounds__(kBlock) void rank_kernel(const int32_t* __restrict_
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int e = tid * kPer + i;
-    local[i] = e < n_experts ? s_tot[e] : 0;
+    local[i] = e < n_experts ? L.tot[e] : 0;
     sum += local[i];
   }
   int total;
-  int run = block_exclusive_scan(sum, s_wave, &total);
+  int run = block_exclusive_scan(sum, L.wave, &total);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int e = tid * kPer + i;
-    if (e < n_experts) s_off[e] = run;
+    if (e < n_experts) L.off[e] = run;
     run += local[i];
   }
-  if (tid == 0) s_off[n_experts] = total;
+  if (tid == 0) L.off[n_experts] = total;
   __syncthreads();
   if (me == 0) {
     for (int e = tid; e < n_experts; e += kBlock) {
-      counts[e] = s_tot[e];
-      offsets[e] = s_off[e];
+      r.counts[e] = L.tot[e];
+      r.offsets[e] = L.off[e];
     }
-    if (tid == 0) offsets[n_experts] = total;
-    for (int g = tid; g <= n_segments; g += kBlock) seg_offsets[g] = s_off[g * per];
+    if (tid == 0) r.offsets[n_experts] = total;
+    for (int g = tid; g <= r.n_segments; g += kBlock) r.seg_offsets[g] = L.off[g * per];
   }
-  if (identity) return;   // the count kernel already wrote the identity maps
+  if (r.identity) return;   // the count kernel already wrote the identity maps
 
-  // 3. this chunk's bucket starts (kept in s_tot, no longer needed)
-  if (sorted) {
-    for (int e = tid; e < n_experts; e += kBlock) s_tot[e] = s_off[e] + s_bef[e];
+  // 3. this chunk's bucket starts (kept in tot, no longer needed)
+  if (r.sorted) {
+    for (int e = tid; e < n_experts; e += kBlock) L.tot[e] = L.off[e] + L.bef[e];
   } else {
-    for (int g = tid; g < n_segments; g += kBlock) {
-      int b = s_off[g * per];
-      for (int e = g * per; e < (g + 1) * per; ++e) b += s_bef[e];
-      s_tot[g] = b;
+    for (int g = tid; g < r.n_segments; g += kBlock) {
+      int b = L.off[g * per];
+      for (int e = g * per; e < (g + 1) * per; ++e) b += L.bef[e];
+      L.tot[g] = b;
     }
   }
 
   // 4. per-wave counts of this chunk, then per-wave starts
-  const int64_t q0 = int64_t(me) * chunk;
-  const int64_t q1 = q0 + chunk < nk ? q0 + chunk : nk;
-  const int sub = (chunk + kWaves - 1) / kWaves;
+  const int64_t q0 = int64_t(me) * r.chunk;
+  const int64_t q1 = q0 + r.chunk < r.nk ? q0 + r.chunk : r.nk;
+  const int sub = (r.chunk + kWaves - 1) / kWaves;
   const int64_t s0 = q0 + int64_t(w) * sub < q1 ? q0 + int64_t(w) * sub : q1;
   const int64_t s1 = s0 + sub < q1 ? s0 + sub : q1;
-  int* mine = wh + w * n_buckets;
-  wave_count(idx, s0, s1, n_experts, sorted, per, mine, nullptr, nullptr);
+  int* mine = L.wh + w * n_buckets;
+  wave_count(r.idx, s0, s1, n_experts, r.sorted, per, mine, nullptr, nullptr);
   __syncthreads();
   for (int b = tid; b < n_buckets; b += kBlock) {
-    int r = s_tot[b];
+    int rr = L.tot[b];
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const int c = wh[ww * n_buckets + b];
-      wh[ww * n_buckets + b] = r;
-      r += c;
+      const int c = L.wh[ww * n_buckets + b];
+      L.wh[ww * n_buckets + b] = rr;
+      rr += c;
     }
   }
   __syncthreads();
-  ordered_walk(idx, s0, s1, n_experts, sorted, per, nbits, mine, dst_pos, src_pair, row_expert);
+  ordered_walk(r.idx, s0, s1, n_experts, r.sorted, per, r.nbits, mine, r.dst_pos, r.src_pair,
+               r.row_expert);
+}
+
+// Block p ranks chunk p.
+__global__ __launch_bounds__(kBlock) void rank_kernel(RankArgs r) {
+  extern __shared__ int lds[];
+  rank_chunk(r, blockIdx.x, rank_lds(lds, r.n_experts, r.sorted ? r.n_experts : r.n_segments));
 }
 
 // ------------------------------------------------------------------ small problems
@@ -376,34 +435,6 @@ __global__ void zero_offsets_kernel(int n_experts, int n_segments, int32_t* coun
 }
 
 // ------------------------------------------------------------------ row copy
-// Token rows are read once per dispatch: non-temporal loads for the 16-byte
-// path, plain loads for the narrow fallback types.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_once(const uint4* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-template <typename V>
-__device__ __forceinline__ V load_once(const V* p) { return *p; }
-
-// An empty asm statement that reads and writes the value's registers: the
-// compiler must have the value in registers (its load waited for) at this point.
-__device__ __forceinline__ void consume(uint4& v) {
-  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
-}
-__device__ __forceinline__ void consume(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
-__device__ __forceinline__ void consume(uint32_t& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void consume(uint16_t& v) {
-  uint32_t t = v;
-  asm volatile("" : "+v"(t));
-  v = uint16_t(t);
-}
-__device__ __forceinline__ void consume(uint8_t& v) {
-  uint32_t t = v;
-  asm volatile("" : "+v"(t));
-  v = uint8_t(t);
-}
-
 // One wave per (token, slice) item; each lane moves U vectors of type V.  The
 // loads use clamped (always valid) indices so they issue back to back.  Lane
 // j < k holds destination j (read with readlane).
@@ -609,10 +640,11 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
                                                     a.status, identity, a.dst_pos, a.src_pair,
                                                     a.row_expert);
     // identity layout: only block 0's offsets are needed
-    rank_kernel<<<identity ? 1 : p.n_chunks, kBlock, 0, stream>>>(
-        a.topk_idx, p.nk, a.n_experts, a.n_segments, p.chunk, p.n_chunks, a.sorted, identity,
-        nbits, hist, a.expert_counts, a.expert_offsets, a.segment_offsets, a.dst_pos,
-        a.src_pair, a.row_expert);
+    const RankArgs r{a.topk_idx, p.nk, a.n_experts, a.n_segments, p.chunk, p.n_chunks, a.sorted,
+                     identity, nbits, hist, a.expert_counts, a.expert_offsets, a.segment_offsets,
+                     a.dst_pos, a.src_pair, a.row_expert};
+    const size_t lds = rank_lds_ints(a.n_experts, n_buckets) * sizeof(int);
+    rank_kernel<<<identity ? 1 : p.n_chunks, kBlock, lds, stream>>>(r);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -36,12 +36,16 @@ class WorkloadConfig:
     top_k: int
     n_segments: int = 1
     sort: object = -1     # -1 auto, 0 unsorted, 1 sorted, 'alternate'
-    sort_cutoff: int = 256
+    sort_cutoff: int = 0  # 0: 24 rows per expert, 24 * E // k (the measured crossover)
     renormalize: bool = True
     zipf_s: float = 0.0
     ffn: int = 0          # > 0: grouped SwiGLU experts, else identity experts
     weight_std: float = 0.02
     note: str = field(default="", compare=False)
+
+    def __post_init__(self):
+        if self.sort_cutoff <= 0:
+            object.__setattr__(self, "sort_cutoff", max(1, 24 * self.n_experts // self.top_k))
 
     def with_tokens(self, n: int) -> "WorkloadConfig":
         return replace(self, n_tokens=n)
