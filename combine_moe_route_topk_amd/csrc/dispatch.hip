@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t* __restrict
       const int e = ev[i];
       if (unsigned(e) < unsigned(n_experts)) atomicAdd(&h[e], 1);
       else bad = true;
-      if (identity) {
+      if (identity == 1) {                // 2: the routing launch wrote the maps
         dst_pos[q] = int32_t(q);
         src_pair[q] = int32_t(q);
         if (row_expert) row_expert[q] = e;
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_meta_kernel(
   const int64_t s1 = s0 + sub < nk ? s0 + sub : nk;
   int* mine = wh + w * n_buckets;
   bool bad = false;
-  if (identity) {
+  if (identity == 1) {                  // 2: the routing launch wrote the maps
     for (int64_t q = s0 + lane; q < s1; q += kWave) {
       dst_pos[q] = int32_t(q);
       src_pair[q] = int32_t(q);
@@ -626,7 +626,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
                                                a.expert_offsets, a.segment_offsets);
     return hipGetLastError();
   }
-  const int identity = (!a.sorted && a.n_segments == 1) ? 1 : 0;
+  // identity layout: 1, or 2 when the routing launch already wrote its maps
+  const int identity = (!a.sorted && a.n_segments == 1) ? (a.maps_done ? 2 : 1) : 0;
   const int n_buckets = a.sorted ? a.n_experts : a.n_segments;
   const int nbits = bits_for(n_buckets);
 
@@ -734,10 +735,12 @@ hipError_t launch_route_dispatch(const RouteArgs& r, const DispatchArgs& a, hipS
     if (identity && a.x && !a.x_scales && (align & 15) == 0) {
       hipError_t err = launch_route_copy_identity(r.logits, a.n_tokens, a.n_experts, a.k,
                                                   r.renormalize, const_cast<int32_t*>(a.topk_idx),
-                                                  r.topk_w, a.x, a.row_bytes, a.rows, stream);
+                                                  r.topk_w, a.x, a.row_bytes, a.rows, a.dst_pos,
+                                                  a.src_pair, a.row_expert, stream);
       if (err != hipSuccess) return err;
       DispatchArgs maps = a;
-      maps.x = nullptr;                     // rows are already in place
+      maps.x = nullptr;                     // rows and maps are already in place
+      maps.maps_done = 1;
       return launch_dispatch(maps, stream);
     }
     hipError_t err = launch_route_topk(r.logits, a.n_tokens, a.n_experts, a.k, r.renormalize,

@@ -46,6 +46,7 @@ struct DispatchArgs {
   int32_t* row_expert;
   void* workspace;
   int32_t* status;          // device word set to 1 on an out-of-range id, or null
+  int maps_done;            // identity layout: the maps are already written
 };
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
@@ -57,11 +58,14 @@ struct RouteArgs {
   float* topk_w;
 };
 // Routing and, side by side in the same launch, the identity-layout row copy
-// (unsorted, one segment): rows [N*k, row_bytes] with row t*k+j = x[t].
-// Requires 16-byte aligned x, rows and row_bytes; n_tokens > 0.
+// (unsorted, one segment): rows [N*k, row_bytes] with row t*k+j = x[t], and
+// the identity maps (dst_pos = src_pair = q, row_expert = the routed expert,
+// row_expert may be null).  Requires 16-byte aligned x, rows and row_bytes;
+// n_tokens > 0.
 hipError_t launch_route_copy_identity(const float* logits, int64_t n_tokens, int n_experts, int k,
                                       int renormalize, int32_t* topk_idx, float* topk_w,
                                       const void* x, int64_t row_bytes, void* rows,
+                                      int32_t* dst_pos, int32_t* src_pair, int32_t* row_expert,
                                       hipStream_t stream);
 size_t route_dispatch_workspace_bytes(int64_t n_tokens, int n_experts, int k, int n_segments);
 hipError_t launch_route_dispatch(const RouteArgs& r, const DispatchArgs& a, hipStream_t stream);

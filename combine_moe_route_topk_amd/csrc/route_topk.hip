@@ -178,12 +178,16 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 // token top_k times with identity inv_order), so the copy needs nothing from
 // the routing: workgroups [0, route_blocks) route (one wave per token) and
 // the rest copy (one wave per (token, 2 KB slice), 16-byte accesses), side by
-// side with no synchronisation between them.
+// side with no synchronisation between them.  The routing waves also write
+// the identity maps of their pairs (dst_pos = src_pair = q, row_expert = the
+// routed expert), leaving only the counts and offsets to the next launch.
 template <int R, int U>
 __global__ __launch_bounds__(256) void route_copy_kernel(
     const float* __restrict__ logits, int64_t n_tokens, int n_experts, int k, int renormalize,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int route_blocks,
-    const uint4* __restrict__ x, int64_t nvec, int n_slices, uint4* __restrict__ rows) {
+    const uint4* __restrict__ x, int64_t nvec, int n_slices, uint4* __restrict__ rows,
+    int32_t* __restrict__ dst_pos, int32_t* __restrict__ src_pair,
+    int32_t* __restrict__ row_expert) {
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
   const int blk = __builtin_amdgcn_readfirstlane(int(blockIdx.x));
@@ -196,8 +200,12 @@ __global__ __launch_bounds__(256) void route_copy_kernel(
     float wt;
     select_token<R>(val, n_experts, k, renormalize, e, wt);
     if (lane < k) {
-      topk_idx[t * k + lane] = e;
-      topk_w[t * k + lane] = wt;
+      const int32_t q = int32_t(t * k + lane);
+      topk_idx[q] = e;
+      topk_w[q] = wt;
+      dst_pos[q] = q;
+      src_pair[q] = q;
+      if (row_expert) row_expert[q] = e;
     }
     return;
   }
@@ -237,6 +245,7 @@ __global__ __launch_bounds__(256) void route_copy_kernel(
 hipError_t launch_route_copy_identity(const float* logits, int64_t n_tokens, int n_experts, int k,
                                       int renormalize, int32_t* topk_idx, float* topk_w,
                                       const void* x, int64_t row_bytes, void* rows,
+                                      int32_t* dst_pos, int32_t* src_pair, int32_t* row_expert,
                                       hipStream_t stream) {
   constexpr int kBlock = 256;
   const int per_block = kBlock / kWave;
@@ -253,11 +262,13 @@ hipError_t launch_route_copy_identity(const float* logits, int64_t n_tokens, int
   if (small)                                                                                 \
     route_copy_kernel<RR, 1><<<grid, kBlock, 0, stream>>>(                                  \
         logits, n_tokens, n_experts, k, renormalize, topk_idx, topk_w, route_blocks,         \
-        static_cast<const uint4*>(x), nvec, n_slices, static_cast<uint4*>(rows));            \
+        static_cast<const uint4*>(x), nvec, n_slices, static_cast<uint4*>(rows), dst_pos,    \
+        src_pair, row_expert);                                                               \
   else                                                                                       \
     route_copy_kernel<RR, 2><<<grid, kBlock, 0, stream>>>(                                  \
         logits, n_tokens, n_experts, k, renormalize, topk_idx, topk_w, route_blocks,         \
-        static_cast<const uint4*>(x), nvec, n_slices, static_cast<uint4*>(rows));            \
+        static_cast<const uint4*>(x), nvec, n_slices, static_cast<uint4*>(rows), dst_pos,    \
+        src_pair, row_expert);                                                               \
   break;
   switch (r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : r <= 8 ? 8 : 16) {
     case 1: MOE_ROUTE_COPY_CASE(1)

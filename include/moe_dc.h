@@ -353,9 +353,14 @@ int moe_gather_swiglu(const void* rows, int64_t n_rows, int64_t hidden,
                       const void* w_gate, const void* w_up, const void* w_down, int64_t ffn,
                       void* y, void* workspace, size_t workspace_bytes, void* stream);
 
-/* moe_gather_swiglu_combine -- moe_gather_swiglu with the weighted top-k
- * sum fused into its down product (the zero-copy combine planned in [MLX-EP]):
- * y is never written.  For every row r whose expert e = row_expert[r] lies in
+/* moe_gather_swiglu_combine -- EXPERIMENTAL: moe_gather_swiglu with the
+ * weighted top-k sum fused into its down product (the zero-copy combine
+ * planned in [MLX-EP]): y is never written.  On MI355X it is slower than the
+ * unfused moe_gather_swiglu + moe_combine pair (the decode layer with
+ * DeepSeek-sized experts: 3.74-3.87 against 3.65-3.77 ms; the atomics cost
+ * more than the y round trip they save) and its output is not bit-stable
+ * between calls; prefer the unfused pair unless the layer is to be added
+ * straight into an fp32 residual.  For every row r whose expert e = row_expert[r] lies in
  * [0, E) and whose pair q (row_pair[r], or r itself when row_pair is null)
  * lies in [0, n_tokens * k):
  *   out[q / k] += topk_w[q] * (W_down[e] h),  h as in moe_gather_swiglu,
