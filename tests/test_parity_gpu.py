@@ -146,6 +146,23 @@ def test_dispatch_duplicate_ids_and_skew(n, e, k, g):
         _dispatch_check(to_dev(idx), e, g, sort, x=rng.standard_normal((n, 8)).astype(np.float32))
 
 
+@pytest.mark.parametrize("n,e,k,g,sort", [
+    (2049, 16, 2, 1, 1), (8192, 8, 2, 1, 1), (4097, 8, 1, 8, 1), (1025, 256, 8, 8, 0),
+    (2048, 1024, 8, 16, 0), (16384, 4, 1, 2, 0), (8000, 16, 2, 4, 1), (8192, 8, 2, 1, 0),
+])
+@pytest.mark.parametrize("skew", [False, True])
+def test_dispatch_few_buckets(n, e, k, g, sort, skew):
+    """4K < N*k <= 16K pairs with at most 16 buckets (experts when sorted,
+    segments when not), where many pairs share each bucket's counters.
+    Uniform and skewed routing (80% of the pairs on one expert)."""
+    rng = np.random.default_rng(n + e + g + sort)
+    idx = np.stack([rng.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    if skew:
+        idx = np.where(rng.uniform(size=(n, k)) < 0.8, 3 % e, idx).astype(np.int32)
+    x = rng.integers(0, 2**16, (n, 24), dtype=np.uint16)
+    _dispatch_check(to_dev(idx), e, g, sort, x=x)
+
+
 @pytest.mark.parametrize("row_elems,dtype", [(3, np.uint16), (5, np.uint16), (6, np.uint16),
                                              (4, np.uint16), (7, np.float32), (1, np.float32),
                                              (2, np.float32)])
@@ -200,6 +217,21 @@ def test_dispatch_reuses_buffers_across_modes():
             assert np.array_equal(to_np(getattr(out, name)), ref[name]), (call, name)
         assert np.array_equal(to_np(out.rows), ref["rows"])
         assert np.array_equal(to_np(out.row_scales), ref["row_scales"])
+
+
+def test_dispatch_validate_mode_reports_bad_ids_few_buckets():
+    """Out-of-range ids are flagged on the multi-workgroup counting path too."""
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, 8, (6000, 2)).astype(np.int32)
+    idx[1234, 1] = 8
+    os.environ["MOE_DC_VALIDATE"] = "1"
+    try:
+        with pytest.raises(moe.MoeError, match="outside"):
+            moe.moe_dispatch(None, to_dev(idx), 8, 1, sort=1)
+        idx[1234, 1] = 7
+        moe.moe_dispatch(None, to_dev(idx), 8, 1, sort=1)
+    finally:
+        del os.environ["MOE_DC_VALIDATE"]
 
 
 def test_dispatch_validate_mode_reports_bad_ids():
