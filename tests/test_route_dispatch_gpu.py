@@ -76,6 +76,25 @@ def test_shapes(n, e, k, g, sort):
     _compare(logits, None, k, g, sort, renorm=False)
 
 
+@pytest.mark.parametrize("n,e,k,g,sort", [
+    (8192, 8, 2, 1, 1),        # the Mixtral-like shape
+    (8192, 8, 2, 4, 0),        # segments (unsorted)
+    (2049, 16, 4, 4, 1), (2049, 16, 4, 2, 0),   # ragged last routing workgroup
+    (32768, 4, 1, 1, 1), (32769, 4, 1, 1, 1),
+    (4097, 2, 2, 2, 1), (5000, 16, 8, 16, 1), (8192, 16, 1, 1, 1),
+    (6000, 8, 3, 1, 1),        # k = 3
+    (3000, 12, 2, 3, 1),       # E = 12
+])
+def test_few_experts(n, e, k, g, sort):
+    """At most 16 experts above the one-workgroup size, ragged token counts,
+    k = 3 and non-power-of-two E; skewed logits make a few experts popular."""
+    rng = np.random.default_rng(n * 7 + e + k)
+    logits = rng.standard_normal((n, e)).astype(np.float32)
+    logits[:, 0] += 1.5
+    x = rng.integers(0, 2**16, (n, 40), dtype=np.uint16)
+    _compare(logits, x, k, g, sort)
+
+
 @pytest.mark.parametrize("cols", [5, 12, 1000])   # 10-, 24- and 2000-byte rows: not 16-byte multiples
 def test_identity_layout_narrow_rows(cols):
     rng = np.random.default_rng(cols)
