@@ -93,9 +93,10 @@ def source_sha(rels):
 class Path:
     """Preallocated buffers and the calls of one step.
 
+    split=False: moe_route_dispatch with the payload | moe_combine (the step
+                 every bench leg times);
     split=True:  moe_route_dispatch (maps only) | moe_scatter_rows | moe_combine,
-                 so the row-copy kernel can be timed on its own (prefill);
-    split=False: moe_route_dispatch with the payload | moe_combine (decode)."""
+                 which puts the row copy in a launch of its own between events."""
 
     def __init__(self, cfg, torch, moe, split=True):
         from workloads import make_inputs
