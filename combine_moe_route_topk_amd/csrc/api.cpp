@@ -184,7 +184,9 @@ int validate_end(int32_t* status, hipStream_t s, int32_t n_experts, const char* 
   hipError_t e = hipMemcpyAsync(&host_status, status, sizeof(int32_t), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_status(e, fn);
-  if (host_status) return fail(MOE_ERR_ARG, "%s: topk_idx holds expert ids outside [0, %d)", fn, n_experts);
+  if (host_status & 1) return fail(MOE_ERR_ARG, "%s: topk_idx holds expert ids outside [0, %d)", fn, n_experts);
+  if (host_status & 2)
+    return fail(MOE_ERR_HIP, "%s: the row copy gave up waiting for positions of its own launch", fn);
   return ok();
 }
 

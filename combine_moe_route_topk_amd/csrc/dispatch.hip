@@ -22,6 +22,17 @@
 //             Multisplit", PPoPP 2016);
 //   copy   -- scatter form: one wave reads a slice of token t's row once and
 //             writes it to the k destination rows dst_pos[t*k + j].
+// With a 16-byte payload, rank and copy share one launch: the rank workgroups
+// come first in the grid, the copy waves load their slice of x at once and
+// then wait only for their own token's k positions.  Each position is its own
+// flag: the count launch sets it to a not-ready value, the rank workgroup
+// replaces it with an atomic store and the copy wave polls it with atomic
+// loads, all relaxed at device scope.  No fence is involved, so no wave
+// invalidates or writes back its L2 (the copy's rows stay cached), and the
+// copy starts without waiting for the slowest rank workgroup.  Waves are
+// dispatched in grid order, so every rank workgroup is resident before any
+// copy wave can wait on it; the wait is bounded all the same (a wave that
+// gives up flags the status word and skips its stores).
 // Small problems (NK <= 4096, at most 256 buckets) run count, scan and rank
 // in one workgroup.  Nothing is read back to the host: NK rows is always the
 // output size.
@@ -39,6 +50,12 @@ constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr int64_t kSmallMaxPairs = 4096;
 constexpr int kSmallMaxBuckets = 256;
+// dst_pos value of a pair whose position is not yet known (valid values are
+// -1 and [0, NK)).
+constexpr int32_t kNotReady = INT32_MIN;
+// Polls of a copy wave before it gives up (each after ~128 cycles of sleep:
+// about 16 ms, three orders of magnitude above a rank workgroup's run time).
+constexpr int kSpinMax = 1 << 18;
 
 __device__ __forceinline__ int bucket_of(int e, int sorted, int per_segment) {
   return sorted ? e : e / per_segment;
@@ -57,7 +74,9 @@ __device__ __forceinline__ uint64_t peer_mask(int key, bool active, int nbits) {
 
 // Walk pairs [s0, s1) in order, 64 at a time, assigning positions from the
 // per-bucket running counters run[] (LDS, private to this wave).  Keys are
-// fetched four steps ahead so their loads overlap.
+// fetched four steps ahead so their loads overlap.  kPublish: dst_pos is
+// written with device-scope atomic stores, for copy waves of the same launch.
+template <bool kPublish>
 __device__ __forceinline__ void ordered_walk(const int32_t* __restrict__ idx, int64_t s0,
                                              int64_t s1, int n_experts, int sorted,
                                              int per_segment, int nbits, int* run,
@@ -90,12 +109,14 @@ __device__ __forceinline__ void ordered_walk(const int32_t* __restrict__ idx, in
         if (rank == 0) run[key] = pos + __popcll(peers);
       }
       __builtin_amdgcn_wave_barrier();
+      if (in) {
+        const int32_t d = ok ? pos : -1;
+        if (kPublish) __hip_atomic_store(dst_pos + q, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else dst_pos[q] = d;
+      }
       if (ok) {
-        dst_pos[q] = pos;
         src_pair[pos] = int32_t(q);
         if (row_expert) row_expert[pos] = e;
-      } else if (in) {
-        dst_pos[q] = -1;
       }
     }
   }
@@ -138,7 +159,8 @@ __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t* __restrict
                                                        int32_t* status, int identity,
                                                        int32_t* __restrict__ dst_pos,
                                                        int32_t* __restrict__ src_pair,
-                                                       int32_t* __restrict__ row_expert) {
+                                                       int32_t* __restrict__ row_expert,
+                                                       int32_t* __restrict__ clear_pos) {
   __shared__ int h[kMaxExperts];
   for (int i = threadIdx.x; i < n_experts; i += kBlock) h[i] = 0;
   __syncthreads();
@@ -165,6 +187,7 @@ __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t* __restrict
         src_pair[q] = int32_t(q);
         if (row_expert) row_expert[q] = e;
       }
+      if (clear_pos) clear_pos[q] = kNotReady;   // published by the rank+copy launch
     }
   }
   if (bad && status) atomicOr(status, 1);
@@ -245,6 +268,7 @@ __device__ __forceinline__ RankLds rank_lds(int* base, int n_experts, int n_buck
   return L;
 }
 
+template <bool kPublish>
 __device__ __forceinline__ void rank_chunk(const RankArgs& r, int me, const RankLds& L) {
   constexpr int kWaves = kBlock / kWave;
   constexpr int kPer = kMaxExperts / kBlock;           // experts per thread in the scan
@@ -349,14 +373,14 @@ __device__ __forceinline__ void rank_chunk(const RankArgs& r, int me, const Rank
     }
   }
   __syncthreads();
-  ordered_walk(r.idx, s0, s1, n_experts, r.sorted, per, r.nbits, mine, r.dst_pos, r.src_pair,
-               r.row_expert);
+  ordered_walk<kPublish>(r.idx, s0, s1, n_experts, r.sorted, per, r.nbits, mine, r.dst_pos,
+                         r.src_pair, r.row_expert);
 }
 
 // Block p ranks chunk p.
 __global__ __launch_bounds__(kBlock) void rank_kernel(RankArgs r) {
   extern __shared__ int lds[];
-  rank_chunk(r, blockIdx.x, rank_lds(lds, r.n_experts, r.sorted ? r.n_experts : r.n_segments));
+  rank_chunk<false>(r, blockIdx.x, rank_lds(lds, r.n_experts, r.sorted ? r.n_experts : r.n_segments));
 }
 
 // ------------------------------------------------------------------ small problems
@@ -421,7 +445,8 @@ __global__ __launch_bounds__(kSmallThreads) void small_meta_kernel(
     }
   }
   __syncthreads();
-  ordered_walk(idx, s0, s1, n_experts, sorted, per, nbits, mine, dst_pos, src_pair, row_expert);
+  ordered_walk<false>(idx, s0, s1, n_experts, sorted, per, nbits, mine, dst_pos, src_pair,
+                      row_expert);
 }
 
 // ------------------------------------------------------------------ N == 0
@@ -475,33 +500,68 @@ __global__ __launch_bounds__(kBlock) void scatter_rows_kernel(const V* __restric
   }
 }
 
-// Payload rows and their block-scale rows in one launch (fp8 workloads):
-// items [0, items_a) copy payload slices, the rest copy scale rows; both with
-// 16-byte accesses.
-template <int U>
-__global__ __launch_bounds__(kBlock) void scatter_pair_kernel(
-    const uint4* __restrict__ xa, int64_t nvec_a, int n_slices_a, uint4* __restrict__ rows_a,
-    const uint4* __restrict__ xb, int64_t nvec_b, int n_slices_b, uint4* __restrict__ rows_b,
-    int64_t n_tokens, int k, const int32_t* __restrict__ dst_pos, int64_t nk) {
+// 16-byte payload rows and, for fp8 workloads, their block-scale rows: items
+// [0, n_tokens * n_slices_a) copy payload slices, the rest (n_slices_b per
+// token, 0 without scales) copy scale rows.
+struct PairCopy {
+  const uint4* xa;
+  int64_t nvec_a;
+  int n_slices_a;
+  uint4* rows_a;
+  const uint4* xb;
+  int64_t nvec_b;
+  int n_slices_b;
+  uint4* rows_b;
+  int64_t n_tokens;
+  int k;
+  int64_t nk;
+};
+
+// Lane j < k: dst_pos[t*k + j] read with a device-scope atomic load (other
+// lanes -1).
+__device__ __forceinline__ int32_t poll_position(const int32_t* dst_pos, int64_t t, int k) {
   const int lane = lane_id();
-  int64_t item = __builtin_amdgcn_readfirstlane(int(blockIdx.x)) * int64_t(kBlock / kWave) +
-                 __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
-  const int64_t items_a = n_tokens * n_slices_a;
-  const uint4* x = xa;
-  uint4* rows = rows_a;
-  int64_t nvec = nvec_a;
-  int n_slices = n_slices_a;
-  if (item >= items_a) {
-    item -= items_a;
-    x = xb;
-    rows = rows_b;
-    nvec = nvec_b;
-    n_slices = n_slices_b;
+  return lane < k ? __hip_atomic_load(dst_pos + t * k + lane, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT)
+                  : -1;
+}
+
+// Poll until no lane holds kNotReady, sleeping between polls; after kSpinMax
+// polls the lanes still waiting give -1 (their rows are skipped) and the
+// status word, if any, gets bit 2.  The loop condition is a ballot, so the
+// wave leaves it together.
+__device__ __forceinline__ int32_t wait_position(int32_t p, const int32_t* dst_pos, int64_t t,
+                                                 int k, int32_t* status) {
+  for (int it = 0; ballot(p == kNotReady) != 0; ++it) {
+    if (it == kSpinMax) {
+      if (status && lane_id() == 0) atomicOr(status, 2);
+      return p == kNotReady ? -1 : p;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    if (p == kNotReady) p = poll_position(dst_pos, t, k);
   }
+  return p;
+}
+
+// One (token, slice) item.  kWait: the positions are published by rank
+// workgroups of the same launch.
+template <int U, bool kWait>
+__device__ __forceinline__ void pair_copy(const PairCopy& c, int64_t item,
+                                          const int32_t* __restrict__ dst_pos, int32_t* status) {
+  const int lane = lane_id();
+  const int64_t items_a = c.n_tokens * c.n_slices_a;
+  const bool second = item >= items_a;       // wave-uniform
+  if (second && c.n_slices_b == 0) return;
+  const uint4* x = second ? c.xb : c.xa;
+  uint4* rows = second ? c.rows_b : c.rows_a;
+  const int64_t nvec = second ? c.nvec_b : c.nvec_a;
+  const int n_slices = second ? c.n_slices_b : c.n_slices_a;
+  if (second) item -= items_a;
   const int64_t t = item / n_slices;
-  if (t >= n_tokens) return;
+  if (t >= c.n_tokens) return;
+  const int k = c.k;
   const int64_t v0 = (item - t * n_slices) * int64_t(kWave * U) + lane;
-  const int my_p = lane < k ? dst_pos[t * k + lane] : -1;
+  int32_t my_p = kWait ? poll_position(dst_pos, t, k) : (lane < k ? dst_pos[t * k + lane] : -1);
   const uint4* src = x + t * nvec;
   uint4 buf[U];
   int64_t vi[U];
@@ -512,13 +572,38 @@ __global__ __launch_bounds__(kBlock) void scatter_pair_kernel(
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) consume(buf[u]);
+  if (kWait) my_p = wait_position(my_p, dst_pos, t, k, status);
   for (int j = 0; j < k; ++j) {
     const int p = __builtin_amdgcn_readlane(my_p, j);
-    if (unsigned(p) >= uint64_t(nk)) continue;
+    if (unsigned(p) >= uint64_t(c.nk)) continue;
     uint4* dst = rows + int64_t(p) * nvec;
 #pragma unroll
     for (int u = 0; u < U; ++u) dst[vi[u]] = buf[u];
   }
+}
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void scatter_pair_kernel(PairCopy c,
+                                                              const int32_t* __restrict__ dst_pos) {
+  const int64_t item = __builtin_amdgcn_readfirstlane(int(blockIdx.x)) * int64_t(kBlock / kWave) +
+                       __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
+  pair_copy<U, false>(c, item, dst_pos, nullptr);
+}
+
+// Rank and copy in one launch: blocks [0, P) rank chunk blockIdx.x and
+// publish its positions; the blocks after them copy (token, slice) items.
+template <int U>
+__global__ __launch_bounds__(kBlock) void rank_scatter_kernel(RankArgs r, PairCopy c,
+                                                              int32_t* status) {
+  extern __shared__ int lds[];
+  const int b = __builtin_amdgcn_readfirstlane(int(blockIdx.x));
+  if (b < r.n_chunks) {
+    rank_chunk<true>(r, b, rank_lds(lds, r.n_experts, r.sorted ? r.n_experts : r.n_segments));
+    return;
+  }
+  const int64_t item = int64_t(b - r.n_chunks) * (kBlock / kWave) +
+                       __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
+  pair_copy<U, true>(c, item, r.dst_pos, status);
 }
 
 template <typename V>
@@ -630,6 +715,42 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
   const int identity = (!a.sorted && a.n_segments == 1) ? (a.maps_done ? 2 : 1) : 0;
   const int n_buckets = a.sorted ? a.n_experts : a.n_segments;
   const int nbits = bits_for(n_buckets);
+  const size_t rank_lds = rank_lds_ints(a.n_experts, n_buckets) * sizeof(int);
+
+  // 16-byte payload (and scale) rows: the copy can share the rank launch
+  constexpr int U = 2;
+  PairCopy c{};
+  bool wide = false;
+  if (a.x) {
+    uint64_t align = uint64_t(a.row_bytes) | reinterpret_cast<uintptr_t>(a.x) |
+                     reinterpret_cast<uintptr_t>(a.rows);
+    if (a.x_scales)
+      align |= uint64_t(a.scale_bytes) | reinterpret_cast<uintptr_t>(a.x_scales) |
+               reinterpret_cast<uintptr_t>(a.row_scales);
+    wide = (align & 15) == 0;
+    if (wide) {
+      c.xa = static_cast<const uint4*>(a.x);
+      c.nvec_a = a.row_bytes / 16;
+      c.n_slices_a = int((c.nvec_a + kWave * U - 1) / (kWave * U));
+      c.rows_a = static_cast<uint4*>(a.rows);
+      if (a.x_scales) {
+        c.xb = reinterpret_cast<const uint4*>(a.x_scales);
+        c.nvec_b = a.scale_bytes / 16;
+        c.n_slices_b = int((c.nvec_b + kWave * U - 1) / (kWave * U));
+        c.rows_b = reinterpret_cast<uint4*>(a.row_scales);
+      }
+      c.n_tokens = a.n_tokens;
+      c.k = a.k;
+      c.nk = p.nk;
+    }
+  }
+  const int per_block = kBlock / kWave;
+  const int64_t copy_blocks =
+      wide ? (a.n_tokens * (c.n_slices_a + c.n_slices_b) + per_block - 1) / per_block : 0;
+  // rank + copy in one launch: general layouts, rank LDS small enough not to
+  // limit the copy's occupancy
+  const bool fused = wide && !identity && !p.small && rank_lds <= 16384 &&
+                     p.n_chunks + copy_blocks <= int64_t(INT32_MAX);
 
   if (p.small) {
     small_meta_kernel<<<1, kSmallThreads, 0, stream>>>(
@@ -639,34 +760,23 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
     int32_t* hist = static_cast<int32_t*>(a.workspace);
     count_kernel<<<p.n_chunks, kBlock, 0, stream>>>(a.topk_idx, p.nk, a.n_experts, p.chunk, hist,
                                                     a.status, identity, a.dst_pos, a.src_pair,
-                                                    a.row_expert);
+                                                    a.row_expert, fused ? a.dst_pos : nullptr);
     // identity layout: only block 0's offsets are needed
     const RankArgs r{a.topk_idx, p.nk, a.n_experts, a.n_segments, p.chunk, p.n_chunks, a.sorted,
                      identity, nbits, hist, a.expert_counts, a.expert_offsets, a.segment_offsets,
                      a.dst_pos, a.src_pair, a.row_expert};
-    const size_t lds = rank_lds_ints(a.n_experts, n_buckets) * sizeof(int);
-    rank_kernel<<<identity ? 1 : p.n_chunks, kBlock, lds, stream>>>(r);
+    if (fused) {
+      rank_scatter_kernel<U><<<unsigned(p.n_chunks + copy_blocks), kBlock, rank_lds, stream>>>(
+          r, c, a.status);
+      return hipGetLastError();
+    }
+    rank_kernel<<<identity ? 1 : p.n_chunks, kBlock, rank_lds, stream>>>(r);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (a.x && a.x_scales) {
-    const uint64_t align = uint64_t(a.row_bytes) | uint64_t(a.scale_bytes) |
-                           reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.rows) |
-                           reinterpret_cast<uintptr_t>(a.x_scales) |
-                           reinterpret_cast<uintptr_t>(a.row_scales);
-    if ((align & 15) == 0) {      // payload and scales in one launch
-      constexpr int U = 2;
-      const int64_t nva = a.row_bytes / 16, nvb = a.scale_bytes / 16;
-      const int nsa = int((nva + kWave * U - 1) / (kWave * U));
-      const int nsb = int((nvb + kWave * U - 1) / (kWave * U));
-      const int64_t items = a.n_tokens * (nsa + nsb);
-      const int per_block = kBlock / kWave;
-      scatter_pair_kernel<U><<<unsigned((items + per_block - 1) / per_block), kBlock, 0, stream>>>(
-          static_cast<const uint4*>(a.x), nva, nsa, static_cast<uint4*>(a.rows),
-          reinterpret_cast<const uint4*>(a.x_scales), nvb, nsb, reinterpret_cast<uint4*>(a.row_scales),
-          a.n_tokens, a.k, a.dst_pos, p.nk);
-      return hipGetLastError();
-    }
+  if (wide) {                      // payload and scales in one launch
+    scatter_pair_kernel<U><<<unsigned(copy_blocks), kBlock, 0, stream>>>(c, a.dst_pos);
+    return hipGetLastError();
   }
   if (a.x) {
     err = launch_scatter(a.x, a.n_tokens, a.row_bytes, a.k, a.dst_pos, p.nk, a.rows, stream);

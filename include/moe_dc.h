@@ -38,7 +38,9 @@
  *     null stream) and returns without waiting.  Outputs are valid in stream
  *     order.  No call synchronises with the host, except in validate mode
  *     (environment variable MOE_DC_VALIDATE=1), where moe_dispatch waits for
- *     its kernels and reports out-of-range expert ids as MOE_ERR_ARG.
+ *     its kernels and reports out-of-range expert ids as MOE_ERR_ARG (and a
+ *     row copy that gave up waiting for its positions, see moe_dispatch, as
+ *     MOE_ERR_HIP).
  *   - Outputs must not alias inputs.
  *   - Errors are returned as a status code before any kernel is launched;
  *     moe_last_error() describes the last failure on the calling thread.  No
@@ -169,7 +171,14 @@ size_t moe_dispatch_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t
  * not given exactly for F8, an unknown dtype or sort value, or x/rows given
  * one without the other; MOE_ERR_UNSUPPORTED for E > MOE_MAX_EXPERTS,
  * k > MOE_MAX_TOPK or NK > INT32_MAX; MOE_ERR_WORKSPACE for a short or
- * misaligned workspace.  N == 0 writes zero counts and offsets. */
+ * misaligned workspace.  N == 0 writes zero counts and offsets.
+ * Launches: with a payload whose row size and addresses (and those of the
+ * scales) are multiples of 16 bytes, outside the identity layout and above
+ * 4096 pairs, positions and row copy share one launch.  dst_pos then serves
+ * as the flag array between them (set to INT32_MIN first, then to each
+ * position, with device-scope atomics).  A copy wave waits for its token's
+ * positions for at most about 2^18 polls (milliseconds); should it ever give
+ * up, it skips those rows, and validate mode reports it. */
 int moe_dispatch(const void* x, const float* x_scales, int32_t dtype,
                  int64_t n_tokens, int64_t hidden,
                  const int32_t* topk_idx, int32_t n_experts, int32_t k, int32_t n_segments,
