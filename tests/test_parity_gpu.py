@@ -246,6 +246,44 @@ def test_dispatch_validate_mode_reports_bad_ids():
         del os.environ["MOE_DC_VALIDATE"]
 
 
+@pytest.mark.parametrize("n,e,k,g,sort,dtype,d", [
+    (5000, 256, 8, 1, 1, "bf16", 64),      # sorted, 40000 pairs
+    (3000, 7, 3, 7, 0, "f32", 12),         # segments (unsorted), 48-byte rows
+    (2049, 64, 2, 1, 1, "bf16", 8),        # 4098 pairs: just above the one-workgroup path
+    (2048, 64, 4, 4, 1, "f8", 512),        # fp8 rows with 16-byte scale rows: both in the launch
+    (2048, 64, 4, 4, 1, "f8", 256),        # 8-byte scale rows: separate row copies
+    (3000, 16, 2, 1, 1, "bf16", 100),      # 200-byte rows (not 16-byte): separate row copy
+])
+def test_rank_and_copy_launch_in_validate_mode(n, e, k, g, sort, dtype, d):
+    """Ranks and row copy sharing one launch (16-byte rows, above 4096 pairs,
+    outside the identity layout), with validate mode on: the call waits and
+    fails if any copy wave gave up waiting for its positions; every map and
+    row is compared with the oracle."""
+    rng = np.random.default_rng(n + e + d)
+    idx = np.stack([rng.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    xs = None
+    if dtype == "f8":
+        x = rng.integers(0, 256, (n, d), dtype=np.uint8)
+        x[(x & 0x7F) == 0x7F] = 0
+        xs = rng.uniform(0.5, 2.0, (n, d // 128)).astype(np.float32)
+    elif dtype == "bf16":
+        x = rng.integers(0, 2**16, (n, d), dtype=np.uint16)
+    else:
+        x = rng.standard_normal((n, d)).astype(np.float32)
+    os.environ["MOE_DC_VALIDATE"] = "1"
+    try:
+        res = moe.moe_dispatch(to_dev(x), to_dev(idx), e, g, sort=sort,
+                               x_scales=None if xs is None else to_dev(xs))
+    finally:
+        del os.environ["MOE_DC_VALIDATE"]
+    ref = od.dispatch(idx, e, g, bool(sort), x=x, x_scales=xs)
+    for name in ("expert_counts", "expert_offsets", "segment_offsets", "src_pair", "dst_pos", "row_expert"):
+        assert np.array_equal(to_np(getattr(res, name)), ref[name]), name
+    assert np.array_equal(to_np(res.rows).view(np.uint8), ref["rows"].view(np.uint8))
+    if xs is not None:
+        assert np.array_equal(to_np(res.row_scales), ref["row_scales"])
+
+
 # ----------------------------------------------------------------- combine
 
 def _combine_case(x_np, idx_dev, w_dev, e, g, sort, out_bf16):
