@@ -275,14 +275,19 @@ __device__ __forceinline__ void mma(f32x16 (&acc)[kTI][kTJ], const Frag& f) {
 }
 
 // Issue order of one slice: 16 MFMAs, the first R each followed by an LDS
-// read, and N direct loads spread evenly between them.
+// read, and N direct loads spread evenly between them, each after its two
+// 64-bit address adds (without the VALU group the scheduler let the loads
+// bunch up behind their address arithmetic).
 template <int R, int N>
 __device__ __forceinline__ void slice_order() {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
     if (q < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // LDS read
-    if ((q * N) / 16 != ((q + 1) * N) / 16) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if ((q * N) / 16 != ((q + 1) * N) / 16) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                   // its address adds
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                   // direct load
+    }
   }
 }
 
@@ -410,7 +415,10 @@ void grouped_gemm_kernel(const uint16_t* __restrict__ A, int64_t n_rows, int K,
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   // stage d lives in slot d % 2; every wave runs the same barrier sequence
-  // kt_n >= 1 stages from k_lo; its parity is the one TAIL says
+  // kt_n >= 1 stages from k_lo; its parity is the one TAIL says.  The main
+  // loop runs four stages per iteration (at its head the first loads wait for
+  // the loop-carried K offset, so fewer heads keep the loads better spread),
+  // then pairs.
   Frag f0, f1;
   load_runs<0, 2 * kLd>(slot0, src, 0);
   stage_barrier();                          // stage 0 landed
@@ -421,6 +429,12 @@ void grouped_gemm_kernel(const uint16_t* __restrict__ A, int64_t n_rows, int K,
     load_runs<0, kLd>(slot1, src, kBK * 2);   // A half of stage 1
     constexpr int kLeft = TAIL == 2 ? 2 : 3;  // stages after the loop of pairs
     int d = 0;
+    for (; d + 4 <= kt_n - kLeft; d += 4) {
+      stage<true, true, true>(acc, f0, f1, slot0, slot1, src, l, d);
+      stage<true, true, true>(acc, f0, f1, slot1, slot0, src, l, d + 1);
+      stage<true, true, true>(acc, f0, f1, slot0, slot1, src, l, d + 2);
+      stage<true, true, true>(acc, f0, f1, slot1, slot0, src, l, d + 3);
+    }
     for (; d < kt_n - kLeft; d += 2) {
       stage<true, true, true>(acc, f0, f1, slot0, slot1, src, l, d);
       stage<true, true, true>(acc, f0, f1, slot1, slot0, src, l, d + 1);
