@@ -83,3 +83,40 @@ def test_noalloc_rejects_sizes_beyond_the_scratch():
     logits = torch.zeros((n, e), dtype=torch.float32, device=DEV)
     with pytest.raises(moe.MoeError, match="static array"):
         moe.moe_route_dispatch_noalloc(logits, None, k, 1, sort=1)
+
+
+@pytest.mark.parametrize("name,sort", [("prefill", 1), ("decode", 0), ("segment", 1)])
+def test_noalloc_under_graph_capture(name, sort):
+    """The callers this entry point is for: captured in a HIP graph with its
+    outputs preallocated (nothing is allocated during capture), replayed four
+    times.  Before each replay every output is clobbered and an eager call of
+    the same entry point on other inputs runs on the same static scratch; each
+    replay must reproduce the eager result bit for bit."""
+    cfg, logits, x, xs = _inputs(name)
+    k, g = cfg.top_k, cfg.n_segments
+    idx, w, res = moe.moe_route_dispatch_noalloc(logits, x, k, g, cfg.renormalize, sort, cfg.sort_cutoff,
+                                                 x_scales=xs)
+    torch.cuda.synchronize()
+    outputs = [idx, w] + [getattr(res, f) for f in FIELDS if getattr(res, f) is not None]
+    eager = [_bits(t).copy() for t in outputs]
+    other_logits = torch.flip(logits, dims=[0]).contiguous()      # a different routing
+
+    def step():
+        moe.moe_route_dispatch_noalloc(logits, x, k, g, cfg.renormalize, sort, cfg.sort_cutoff,
+                                       x_scales=xs, topk_idx=idx, topk_w=w, out=res)
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        for t in outputs:
+            t.zero_()
+        moe.moe_route_dispatch_noalloc(other_logits, x, k, g, cfg.renormalize, sort, cfg.sort_cutoff,
+                                       x_scales=xs)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, t in enumerate(outputs):
+            assert np.array_equal(_bits(t), eager[i]), (rep, i)
