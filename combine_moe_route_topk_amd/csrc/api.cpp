@@ -42,6 +42,17 @@ bool validate_mode() {
   return v && v[0] == '1';
 }
 
+// Test hook: MOE_DC_SPIN_LIMIT=<n> caps the polls of a copy wave that waits for
+// positions of its own launch (so tests can force the give-up path); unset or
+// malformed: the library default.
+int spin_limit() {
+  const char* v = std::getenv("MOE_DC_SPIN_LIMIT");
+  if (!v || !*v) return -1;
+  char* end = nullptr;
+  const long n = std::strtol(v, &end, 10);
+  return (end && *end == '\0' && n >= 0 && n < (1L << 30)) ? int(n) : -1;
+}
+
 int check_routing_sizes(const char* fn, int64_t n_tokens, int32_t n_experts, int32_t k) {
   if (n_tokens < 0) return fail(MOE_ERR_ARG, "%s: n_tokens < 0", fn);
   if (n_experts < 1) return fail(MOE_ERR_ARG, "%s: n_experts < 1", fn);
@@ -167,6 +178,7 @@ int prepare_dispatch(const char* fn, const void* x, const float* x_scales, int32
   a.dst_pos = dst_pos;
   a.row_expert = row_expert;
   a.workspace = workspace;
+  a.spin_limit = spin_limit();
   return MOE_OK;
 }
 

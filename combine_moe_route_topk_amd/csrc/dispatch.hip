@@ -53,8 +53,9 @@ constexpr int kSmallMaxBuckets = 256;
 // dst_pos value of a pair whose position is not yet known (valid values are
 // -1 and [0, NK)).
 constexpr int32_t kNotReady = INT32_MIN;
-// Polls of a copy wave before it gives up (each after ~128 cycles of sleep:
-// about 16 ms, three orders of magnitude above a rank workgroup's run time).
+// Polls of a copy wave before it gives up by default (each after ~128 cycles
+// of sleep and a memory round trip: milliseconds, three orders of magnitude
+// above a rank workgroup's run time).
 constexpr int kSpinMax = 1 << 18;
 
 __device__ __forceinline__ int bucket_of(int e, int sorted, int per_segment) {
@@ -515,6 +516,7 @@ struct PairCopy {
   int64_t n_tokens;
   int k;
   int64_t nk;
+  int spin_max;          // polls before a waiting copy wave gives up
 };
 
 // Lane j < k: dst_pos[t*k + j] read with a device-scope atomic load (other
@@ -526,14 +528,14 @@ __device__ __forceinline__ int32_t poll_position(const int32_t* dst_pos, int64_t
                   : -1;
 }
 
-// Poll until no lane holds kNotReady, sleeping between polls; after kSpinMax
+// Poll until no lane holds kNotReady, sleeping between polls; after spin_max
 // polls the lanes still waiting give -1 (their rows are skipped) and the
 // status word, if any, gets bit 2.  The loop condition is a ballot, so the
 // wave leaves it together.
 __device__ __forceinline__ int32_t wait_position(int32_t p, const int32_t* dst_pos, int64_t t,
-                                                 int k, int32_t* status) {
+                                                 int k, int32_t* status, int spin_max) {
   for (int it = 0; ballot(p == kNotReady) != 0; ++it) {
-    if (it == kSpinMax) {
+    if (it >= spin_max) {
       if (status && lane_id() == 0) atomicOr(status, 2);
       return p == kNotReady ? -1 : p;
     }
@@ -572,7 +574,7 @@ __device__ __forceinline__ void pair_copy(const PairCopy& c, int64_t item,
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) consume(buf[u]);
-  if (kWait) my_p = wait_position(my_p, dst_pos, t, k, status);
+  if (kWait) my_p = wait_position(my_p, dst_pos, t, k, status, c.spin_max);
   for (int j = 0; j < k; ++j) {
     const int p = __builtin_amdgcn_readlane(my_p, j);
     if (unsigned(p) >= uint64_t(c.nk)) continue;
@@ -742,6 +744,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
       c.n_tokens = a.n_tokens;
       c.k = a.k;
       c.nk = p.nk;
+      c.spin_max = a.spin_limit >= 0 ? a.spin_limit : kSpinMax;
     }
   }
   const int per_block = kBlock / kWave;

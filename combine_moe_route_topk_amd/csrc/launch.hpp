@@ -47,6 +47,8 @@ struct DispatchArgs {
   void* workspace;
   int32_t* status;          // device word set to 1 on an out-of-range id, or null
   int maps_done;            // identity layout: the maps are already written
+  int spin_limit = -1;      // polls before a copy wave of the shared rank + copy launch
+                            // gives up (< 0: the default)
 };
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);

@@ -178,7 +178,9 @@ size_t moe_dispatch_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t
  * as the flag array between them (set to INT32_MIN first, then to each
  * position, with device-scope atomics).  A copy wave waits for its token's
  * positions for at most about 2^18 polls (milliseconds); should it ever give
- * up, it skips those rows, and validate mode reports it. */
+ * up, it skips those rows, and validate mode reports it.  (Test hook: the
+ * environment variable MOE_DC_SPIN_LIMIT=<n> sets that limit, so tests can
+ * force the give-up path.) */
 int moe_dispatch(const void* x, const float* x_scales, int32_t dtype,
                  int64_t n_tokens, int64_t hidden,
                  const int32_t* topk_idx, int32_t n_experts, int32_t k, int32_t n_segments,

@@ -284,6 +284,45 @@ def test_rank_and_copy_launch_in_validate_mode(n, e, k, g, sort, dtype, d):
         assert np.array_equal(to_np(res.row_scales), ref["row_scales"])
 
 
+def test_rank_and_copy_give_up_path_is_reported():
+    """The copy waves of the shared rank + copy launch wait a bounded number of
+    polls for their positions.  With the limit forced to 0 from the host
+    (MOE_DC_SPIN_LIMIT, a test hook), waves that find their positions not yet
+    published give up at once: the launch still ends normally, those rows are
+    skipped, and validate mode reports it (at the prefill size the first copy
+    waves poll long before the rank workgroups finish, so this is all but
+    certain; a call where no wave had to wait must then be exact).  The next
+    call, with the default limit, is exact again."""
+    cfg = CONFIGS["prefill"]
+    inp = make_inputs(cfg)
+    idx, _ = moe.moe_route_topk(to_dev(inp["logits"]), cfg.top_k)
+    x = to_dev(inp["x"])
+    ref = od.dispatch(to_np(idx), cfg.n_experts, 1, True)
+    rng = np.random.default_rng(3)
+    sample = rng.integers(0, cfg.n_tokens * cfg.top_k, 4000)
+    xh = inp["x"]
+
+    def exact(res):
+        for name in ("expert_counts", "expert_offsets", "src_pair", "dst_pos", "row_expert"):
+            assert np.array_equal(to_np(getattr(res, name)), ref[name]), name
+        rows = res.rows[torch.from_numpy(sample).to(DEV)]
+        assert np.array_equal(to_np(rows), xh[ref["src_pair"][sample] // cfg.top_k])
+
+    os.environ["MOE_DC_VALIDATE"] = "1"
+    try:
+        os.environ["MOE_DC_SPIN_LIMIT"] = "0"
+        try:
+            res = moe.moe_dispatch(x, idx, cfg.n_experts, 1, sort=1)
+            exact(res)
+        except moe.MoeError as err:
+            assert "gave up" in str(err)
+        finally:
+            del os.environ["MOE_DC_SPIN_LIMIT"]
+        exact(moe.moe_dispatch(x, idx, cfg.n_experts, 1, sort=1))
+    finally:
+        del os.environ["MOE_DC_VALIDATE"]
+
+
 # ----------------------------------------------------------------- combine
 
 def _combine_case(x_np, idx_dev, w_dev, e, g, sort, out_bf16):
