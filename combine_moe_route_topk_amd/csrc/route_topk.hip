@@ -55,6 +55,27 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
 }
 
+// One step of a DPP sum: lanes outside ROW_MASK and lanes whose source is out
+// of range add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_sum_step(float v) {
+  const float o = __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
+  return v + o;
+}
+
+// Sum over the wave with DPP row operations (a tree of depth 6), returned
+// uniformly (from lane 63).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = dpp_sum_step<kQuadPerm1032, 0xF>(v);
+  v = dpp_sum_step<kQuadPerm2301, 0xF>(v);
+  v = dpp_sum_step<kRowHalfMirror, 0xF>(v);
+  v = dpp_sum_step<kRowMirror, 0xF>(v);
+  v = dpp_sum_step<kRowBcast15, 0xA>(v);
+  v = dpp_sum_step<kRowBcast31, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // exp(a - b) without the rounding error of the fp32 difference.  Knuth's
 // two-sum splits a - b exactly into s + r with s = fl(a - b) and |r| <= ulp(s)/2;
 // then exp(a - b) = exp(s) * exp(r) = exp(s) * (1 + r) to far below fp32
@@ -135,17 +156,18 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
     }
   }
 
-  const float top = __shfl(my_v, 0);                  // slot 0 is the maximum
+  // slot 0 is the maximum
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
   const float num = lane < k ? exp_diff(my_v, top) : 0.f;
   float den;
   if (renormalize) {
-    den = wave_reduce_sum(num);
+    den = wave_sum_f32(num);
   } else {
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (lane + r * kWave < n_experts) s += exp_diff(val[r], top);
-    den = wave_reduce_sum(s);
+    den = wave_sum_f32(s);
   }
   out_e = my_e;
   out_w = num / den;
