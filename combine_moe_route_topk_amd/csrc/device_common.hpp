@@ -56,6 +56,27 @@ __device__ __forceinline__ float wave_reduce_sum(float v) {
   return v;
 }
 
+// One step of a DPP integer scan: lanes outside ROW_MASK and lanes whose
+// source is out of range add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_add_step(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the wave with DPP row operations (no LDS
+// crossbar round trips): shifts by 1, 2, 4, 8 within each 16-lane row, then
+// row 0's and row 2's last lanes are broadcast into rows 1 and 3, then lane
+// 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v = dpp_add_step<0x111, 0xF>(v);    // row_shr:1
+  v = dpp_add_step<0x112, 0xF>(v);    // row_shr:2
+  v = dpp_add_step<0x114, 0xF>(v);    // row_shr:4
+  v = dpp_add_step<0x118, 0xF>(v);    // row_shr:8
+  v = dpp_add_step<0x142, 0xA>(v);    // row_bcast:15
+  v = dpp_add_step<0x143, 0xC>(v);    // row_bcast:31
+  return v;
+}
+
 // Exclusive scan of one int per thread over a workgroup of up to 1024
 // threads; returns the exclusive prefix and writes the total to *total.
 // s_wave holds (waves + 1) ints of LDS; every thread of the workgroup calls it.
@@ -63,12 +84,7 @@ __device__ inline int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int nw = blockDim.x / kWave;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_inclusive_scan(v);
   if (lane == kWave - 1) s_wave[w] = incl;
   __syncthreads();
   if (threadIdx.x == 0) {
