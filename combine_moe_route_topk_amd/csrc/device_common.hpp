@@ -77,6 +77,34 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// Inclusive running maximum over the wave, for values >= 0 (the same DPP
+// steps as the scan; out-of-range sources read 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_max_step_nonneg(int v) {
+  const int o = __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ int wave_inclusive_max_nonneg(int v) {
+  v = dpp_max_step_nonneg<0x111, 0xF>(v);
+  v = dpp_max_step_nonneg<0x112, 0xF>(v);
+  v = dpp_max_step_nonneg<0x114, 0xF>(v);
+  v = dpp_max_step_nonneg<0x118, 0xF>(v);
+  v = dpp_max_step_nonneg<0x142, 0xA>(v);
+  v = dpp_max_step_nonneg<0x143, 0xC>(v);
+  return v;
+}
+
+// The value of lane l - 1 in lane l (lane 0 reads `first`).
+__device__ __forceinline__ int wave_shift_up1(int v, int first) {
+  const int o = __builtin_amdgcn_update_dpp(0, v, 0x138, 0xF, 0xF, true);   // wave_shr:1
+  return lane_id() == 0 ? first : o;
+}
+
+// Value of lane `src` (wave-uniform) in every lane.
+__device__ __forceinline__ int lane_value(int v, int src) {
+  return __builtin_amdgcn_readlane(v, src);
+}
+
 // Exclusive scan of one int per thread over a workgroup of up to 1024
 // threads; returns the exclusive prefix and writes the total to *total.
 // s_wave holds (waves + 1) ints of LDS; every thread of the workgroup calls it.

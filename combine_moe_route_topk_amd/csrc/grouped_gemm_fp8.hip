@@ -71,24 +71,19 @@ __device__ Fp8Tile find_fp8_tile(int m_idx, const int32_t* __restrict__ offs, in
       hi = int(b < lo ? lo : (b > n_rows ? n_rows : b));
       nt = (hi - lo + kTM - 1) / kTM;
     }
-    int incl = nt;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int v = __shfl_up(incl, d);
-      if (lane >= d) incl += v;
-    }
+    const int incl = wave_inclusive_scan(nt);         // DPP, no LDS round trips
     const int excl = incl - nt;
     const uint64_t own = ballot(nt > 0 && m_idx >= base + excl && m_idx < base + incl);
     if (own) {
       const int src = __ffsll((unsigned long long)own) - 1;
-      const int lo_s = __shfl(lo, src), hi_s = __shfl(hi, src), ex_s = __shfl(excl, src);
+      const int lo_s = lane_value(lo, src), hi_s = lane_value(hi, src), ex_s = lane_value(excl, src);
       t.expert = c + src;
       t.row0 = lo_s + int64_t(m_idx - base - ex_s) * kTM;
       t.row_end = hi_s;
       t.valid = true;
       return t;
     }
-    base += __shfl(incl, kWave - 1);
+    base += lane_value(incl, kWave - 1);
   }
   return t;
 }

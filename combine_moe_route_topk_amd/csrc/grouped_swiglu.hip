@@ -131,26 +131,23 @@ __device__ TileInfo find_row_tile(int m, const int32_t* __restrict__ offs, int n
 
 // Number of real row tiles under the same ranges, 64 experts at a time: hi_e =
 // min(R, max(lo_0, offs[1..e+1])) is a running maximum, so each chunk takes an
-// inclusive max-scan across the wave.
+// inclusive max-scan across the wave (DPP row operations; the clamp into
+// [lo_0, R] commutes with the running maximum, so it is applied first).
 __device__ int count_row_tiles(const int32_t* __restrict__ offs, int n_experts, int64_t n_rows) {
   const int lane = lane_id();
-  long long carry = offs[0] < 0 ? 0 : (offs[0] > n_rows ? n_rows : offs[0]);
+  const int R = int(n_rows);                  // NK <= INT32_MAX rows
+  int carry = offs[0] < 0 ? 0 : (offs[0] > R ? R : offs[0]);
   int total = 0;
   for (int c = 0; c < n_experts; c += kWave) {
     const int e = c + lane;
-    long long v = e < n_experts ? (long long)offs[e + 1] : carry;
-    for (int d = 1; d < kWave; d <<= 1) {
-      const long long o = __shfl_up(v, d);
-      if (lane >= d) v = o > v ? o : v;
-    }
-    long long hi = v > carry ? v : carry;
-    hi = hi > n_rows ? n_rows : hi;
-    long long lo = __shfl_up(hi, 1);
-    if (lane == 0) lo = carry;
-    int nt = e < n_experts ? int((hi - lo + kBM - 1) / kBM) : 0;
-    for (int d = kWave / 2; d >= 1; d >>= 1) nt += __shfl_xor(nt, d);
-    total += nt;
-    carry = __shfl(hi, kWave - 1);
+    int v = e < n_experts ? offs[e + 1] : carry;
+    v = v > R ? R : v;
+    v = v < carry ? carry : v;
+    const int hi = wave_inclusive_max_nonneg(v);
+    const int lo = wave_shift_up1(hi, carry);
+    const int nt = e < n_experts ? (hi - lo + kBM - 1) / kBM : 0;
+    total += lane_value(wave_inclusive_scan(nt), kWave - 1);
+    carry = lane_value(hi, kWave - 1);
   }
   return __builtin_amdgcn_readfirstlane(total);
 }
