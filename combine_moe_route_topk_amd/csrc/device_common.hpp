@@ -40,22 +40,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16_rne(lo)) | (uint32_t(f32_to_bf16_rne(hi)) << 16);
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_reduce_max(T v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    T o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-__device__ __forceinline__ float wave_reduce_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
 // One step of a DPP integer scan: lanes outside ROW_MASK and lanes whose
 // source is out of range add 0.
 template <int CTRL, int ROW_MASK>
