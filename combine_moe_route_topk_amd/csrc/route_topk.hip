@@ -3,13 +3,14 @@
 // Produces expert_indices [N, k] (the routing output flattened and sorted by
 // the sorted gather branch of "backends/mlx: runtime MoE expert-sort for
 // decode (issue #20554)", author's follow-up "Handler fixes") and fp32
-// weights.  Each lane holds R = ceil(E/64) logits of experts lane + 64*r as
+// weights.  Each lane holds R = ceil(E/64) logits of the contiguous experts
+// R*lane + r (one 16-byte load per lane when the row allows) as
 // order-preserving unsigned images of their values (-0.0 folded onto +0.0),
 // and tracks its own best (largest value, lowest expert on ties).  Each of
 // the k rounds takes the wave maximum of the lanes' bests with DPP row
-// operations and a ballot of the lanes that hold it; the lowest expert id
-// among them wins (a second reduction runs only when values tie).  The winner
-// retires its key.
+// operations and a ballot of the lanes that hold it; since lower lanes hold
+// lower experts, the lowest such lane holds the lowest expert with that value
+// and wins.  The winner retires its key.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -90,24 +91,25 @@ __device__ __forceinline__ float exp_diff(float a, float b) {
   return fmaf(e, r, e);
 }
 
-__device__ __forceinline__ int wave_min_i32(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const int o = __shfl_xor(v, off);
-    v = o < v ? o : v;
-  }
-  return v;
-}
-
-// Loads one token's logits: lane l holds experts l + 64 r.
+// Loads one token's logits: lane l holds experts R*l + r, with 16-byte loads
+// when R is a multiple of 4, the row is 16-byte aligned and the lane's
+// experts all exist (the choice is uniform over the lanes that take it).
 template <int R>
 __device__ __forceinline__ void load_token(const float* __restrict__ row, int n_experts,
                                            float (&val)[R]) {
-  const int lane = lane_id();
+  const int e0 = lane_id() * R;
+  if (R % 4 == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0 && e0 + R <= n_experts) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = lane + r * kWave;
-    val[r] = e < n_experts ? row[e] : 0.f;
+    for (int r = 0; r < R; r += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + e0 + r);
+      val[r] = v.x;
+      val[r + 1] = v.y;
+      val[r + 2] = v.z;
+      val[r + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) val[r] = e0 + r < n_experts ? row[e0 + r] : 0.f;
   }
 }
 
@@ -120,7 +122,7 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
   uint32_t ov[R];
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    ov[r] = lane + r * kWave < n_experts ? ordered_bits(val[r]) : 0u;   // 0: below every value
+    ov[r] = lane * R + r < n_experts ? ordered_bits(val[r]) : 0u;   // 0: below every value
   auto local_best = [&](uint32_t& bo, int& br) {
     bo = ov[0];
     br = 0;
@@ -137,17 +139,13 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
   for (int j = 0; j < k; ++j) {
     const uint32_t m = wave_max_u32(best_o);
     const uint64_t cand = ballot(best_o == m);
-    int win;
-    if (__popcll(cand) == 1) {
-      const int wl = __ffsll((unsigned long long)cand) - 1;
-      win = wl + kWave * __builtin_amdgcn_readlane(best_r, wl);
-    } else {
-      win = wave_min_i32(best_o == m ? lane + kWave * best_r : 0x7fffffff);
-    }
-    if ((win & (kWave - 1)) == lane) {
+    const int wl = __ffsll((unsigned long long)cand) - 1;        // lowest lane: lowest expert
+    const int wr = __builtin_amdgcn_readlane(best_r, wl);
+    const int win = wl * R + wr;
+    if (lane == wl) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (r == (win >> 6)) ov[r] = 0u;
+        if (r == wr) ov[r] = 0u;
       local_best(best_o, best_r);
     }
     if (lane == j) {
@@ -166,7 +164,7 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (lane + r * kWave < n_experts) s += exp_diff(val[r], top);
+      if (lane * R + r < n_experts) s += exp_diff(val[r], top);
     den = wave_sum_f32(s);
   }
   out_e = my_e;
