@@ -6,7 +6,8 @@
 // weights.  Each lane holds R = ceil(E/64) logits of the contiguous experts
 // R*lane + r (one 16-byte load per lane when the row allows) as
 // order-preserving unsigned images of their values (-0.0 folded onto +0.0),
-// and tracks its own best (largest value, lowest expert on ties).  Each of
+// and tracks its own best (largest value, lowest expert on ties; for R <= 4
+// the lane sorts its keys once and pops its head when it wins).  Each of
 // the k rounds takes the wave maximum of the lanes' bests with DPP row
 // operations and a ballot of the lanes that hold it; since lower lanes hold
 // lower experts, the lowest such lane holds the lowest expert with that value
@@ -123,38 +124,80 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
 #pragma unroll
   for (int r = 0; r < R; ++r)
     ov[r] = lane * R + r < n_experts ? ordered_bits(val[r]) : 0u;   // 0: below every value
-  auto local_best = [&](uint32_t& bo, int& br) {
-    bo = ov[0];
-    br = 0;
-#pragma unroll
-    for (int r = 1; r < R; ++r)
-      if (ov[r] > bo) { bo = ov[r]; br = r; }         // strict: lower r wins ties
-  };
-  uint32_t best_o;
-  int best_r;
-  local_best(best_o, best_r);
-
   int my_e = 0;          // lane j < k ends up holding slot j
   float my_v = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const uint32_t m = wave_max_u32(best_o);
-    const uint64_t cand = ballot(best_o == m);
-    const int wl = __ffsll((unsigned long long)cand) - 1;        // lowest lane: lowest expert
-    const int wr = __builtin_amdgcn_readlane(best_r, wl);
-    const int win = wl * R + wr;
-    if (lane == wl) {
+  if constexpr (R <= 4) {
+    // Each lane sorts its keys once (value descending, lower expert first on
+    // ties: a strict total order, so any compare-exchange network sorts
+    // them); a round's winner then pops its head, with no re-scan and no
+    // branch.
+    uint32_t key[R];
+    int rid[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (r == wr) ov[r] = 0u;
-      local_best(best_o, best_r);
+    for (int r = 0; r < R; ++r) {
+      key[r] = ov[r];
+      rid[r] = r;
     }
-    if (lane == j) {
-      my_e = win;
-      my_v = value_of_ordered(m);
+    auto cex = [&](int a, int b) {      // positions a < b: put the larger pair first
+      const bool sw = key[b] > key[a] || (key[b] == key[a] && rid[b] < rid[a]);
+      const uint32_t ka = key[a], kb = key[b];
+      const int ra = rid[a], rb = rid[b];
+      key[a] = sw ? kb : ka;
+      key[b] = sw ? ka : kb;
+      rid[a] = sw ? rb : ra;
+      rid[b] = sw ? ra : rb;
+    };
+    if constexpr (R == 2) cex(0, 1);
+    if constexpr (R == 4) {
+      cex(0, 1); cex(2, 3); cex(0, 2); cex(1, 3); cex(1, 2);
+    }
+    for (int j = 0; j < k; ++j) {
+      const uint32_t m = wave_max_u32(key[0]);
+      const uint64_t cand = ballot(key[0] == m);
+      const int wl = __ffsll((unsigned long long)cand) - 1;    // lowest lane: lowest expert
+      const int win = wl * R + __builtin_amdgcn_readlane(rid[0], wl);
+      const bool me = lane == wl;
+#pragma unroll
+      for (int r = 0; r + 1 < R; ++r) {
+        key[r] = me ? key[r + 1] : key[r];
+        rid[r] = me ? rid[r + 1] : rid[r];
+      }
+      key[R - 1] = me ? 0u : key[R - 1];
+      if (lane == j) {
+        my_e = win;
+        my_v = value_of_ordered(m);
+      }
+    }
+  } else {
+    auto local_best = [&](uint32_t& bo, int& br) {
+      bo = ov[0];
+      br = 0;
+#pragma unroll
+      for (int r = 1; r < R; ++r)
+        if (ov[r] > bo) { bo = ov[r]; br = r; }         // strict: lower r wins ties
+    };
+    uint32_t best_o;
+    int best_r;
+    local_best(best_o, best_r);
+    for (int j = 0; j < k; ++j) {
+      const uint32_t m = wave_max_u32(best_o);
+      const uint64_t cand = ballot(best_o == m);
+      const int wl = __ffsll((unsigned long long)cand) - 1;      // lowest lane: lowest expert
+      const int wr = __builtin_amdgcn_readlane(best_r, wl);
+      const int win = wl * R + wr;
+      if (lane == wl) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (r == wr) ov[r] = 0u;
+        local_best(best_o, best_r);
+      }
+      if (lane == j) {
+        my_e = win;
+        my_v = value_of_ordered(m);
+      }
     }
   }
 
-  // slot 0 is the maximum
   const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
   const float num = lane < k ? exp_diff(my_v, top) : 0.f;
   float den;
