@@ -124,8 +124,8 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
 #pragma unroll
   for (int r = 0; r < R; ++r)
     ov[r] = lane * R + r < n_experts ? ordered_bits(val[r]) : 0u;   // 0: below every value
-  int my_e = 0;          // lane j < k ends up holding slot j
-  float my_v = 0.f;
+  int my_e = 0;          // lane j < k ends up holding slot j ...
+  uint32_t my_o = 0u;    // ... and its key (decoded to the logit after the rounds)
   if constexpr (R <= 4) {
     // Each lane sorts its keys once (value descending, lower expert first on
     // ties: a strict total order, so any compare-exchange network sorts
@@ -153,8 +153,8 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
     }
     for (int j = 0; j < k; ++j) {
       const uint32_t m = wave_max_u32(key[0]);
-      const uint64_t cand = ballot(key[0] == m);
-      const int wl = __ffsll((unsigned long long)cand) - 1;    // lowest lane: lowest expert
+      const uint64_t cand = ballot(key[0] == m);                // never empty
+      const int wl = int(__builtin_ctzll(cand));                // lowest lane: lowest expert
       const int win = wl * R + __builtin_amdgcn_readlane(rid[0], wl);
       const bool me = lane == wl;
 #pragma unroll
@@ -165,7 +165,7 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
       key[R - 1] = me ? 0u : key[R - 1];
       if (lane == j) {
         my_e = win;
-        my_v = value_of_ordered(m);
+        my_o = m;
       }
     }
   } else {
@@ -181,8 +181,8 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
     local_best(best_o, best_r);
     for (int j = 0; j < k; ++j) {
       const uint32_t m = wave_max_u32(best_o);
-      const uint64_t cand = ballot(best_o == m);
-      const int wl = __ffsll((unsigned long long)cand) - 1;      // lowest lane: lowest expert
+      const uint64_t cand = ballot(best_o == m);                // never empty
+      const int wl = int(__builtin_ctzll(cand));                // lowest lane: lowest expert
       const int wr = __builtin_amdgcn_readlane(best_r, wl);
       const int win = wl * R + wr;
       if (lane == wl) {
@@ -193,11 +193,13 @@ __device__ __forceinline__ void select_token(const float (&val)[R], int n_expert
       }
       if (lane == j) {
         my_e = win;
-        my_v = value_of_ordered(m);
+        my_o = m;
       }
     }
   }
 
+  const float my_v = value_of_ordered(my_o);
+  // slot 0 holds the maximum
   const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
   const float num = lane < k ? exp_diff(my_v, top) : 0.f;
   float den;
