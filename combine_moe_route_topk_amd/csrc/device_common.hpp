@@ -99,14 +99,11 @@ __device__ inline int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int incl = wave_inclusive_scan(v);
   if (lane == kWave - 1) s_wave[w] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < nw; ++i) {
-      const int c = s_wave[i];
-      s_wave[i] = run;
-      run += c;
-    }
-    s_wave[nw] = run;
+  if (w == 0) {                       // the per-wave totals, scanned by wave 0
+    const int t = lane < nw ? s_wave[lane] : 0;
+    const int inc = wave_inclusive_scan(t);
+    if (lane < nw) s_wave[lane] = inc - t;
+    if (lane == nw - 1) s_wave[nw] = inc;
   }
   __syncthreads();
   const int excl = s_wave[w] + incl - v;
