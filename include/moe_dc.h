@@ -173,8 +173,9 @@ size_t moe_dispatch_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t
  * k > MOE_MAX_TOPK or NK > INT32_MAX; MOE_ERR_WORKSPACE for a short or
  * misaligned workspace.  N == 0 writes zero counts and offsets.
  * Launches: with a payload whose row size and addresses (and those of the
- * scales) are multiples of 16 bytes, outside the identity layout and above
- * 4096 pairs, positions and row copy share one launch.  dst_pos then serves
+ * scales) are multiples of 16 bytes, outside the identity layout, above 4096
+ * pairs and with the rank's LDS within 16 KB (E <= 584 sorted), positions and
+ * row copy share one launch.  dst_pos then serves
  * as the flag array between them (set to INT32_MIN first, then to each
  * position, with device-scope atomics).  A copy wave waits for its token's
  * positions for at most about 2^18 polls (milliseconds); should it ever give
