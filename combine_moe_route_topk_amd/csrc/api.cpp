@@ -280,8 +280,18 @@ int route_dispatch_impl(const char* fn, const float* logits, int32_t renormalize
     if (e != hipSuccess) return hip_status(e, fn);
   }
   if (sorted_used) *sorted_used = a.sorted;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // validate mode: moe_route_dispatch only (its host copy and wait have no
+  // place in the allocation-free variant)
+  const bool validate = !static_scratch && validate_mode();
+  if (validate) {
+    a.status = validate_begin(workspace, need, s, &rc, fn);
+    if (rc) return rc;
+  }
   moe::RouteArgs r{logits, renormalize ? 1 : 0, topk_w};
-  return hip_status(moe::launch_route_dispatch(r, a, static_cast<hipStream_t>(stream)), fn);
+  rc = hip_status(moe::launch_route_dispatch(r, a, s), fn);
+  if (rc || !validate) return rc;
+  return validate_end(a.status, s, n_experts, fn);
 }
 
 }  // namespace

@@ -37,10 +37,10 @@
  *   - Every call enqueues its kernels on `stream` (a hipStream_t; NULL is the
  *     null stream) and returns without waiting.  Outputs are valid in stream
  *     order.  No call synchronises with the host, except in validate mode
- *     (environment variable MOE_DC_VALIDATE=1), where moe_dispatch waits for
- *     its kernels and reports out-of-range expert ids as MOE_ERR_ARG (and a
- *     row copy that gave up waiting for its positions, see moe_dispatch, as
- *     MOE_ERR_HIP).
+ *     (environment variable MOE_DC_VALIDATE=1), where moe_dispatch and
+ *     moe_route_dispatch wait for their kernels and report out-of-range
+ *     expert ids as MOE_ERR_ARG (and a row copy that gave up waiting for its
+ *     positions, see moe_dispatch, as MOE_ERR_HIP).
  *   - Outputs must not alias inputs.
  *   - Errors are returned as a status code before any kernel is launched;
  *     moe_last_error() describes the last failure on the calling thread.  No
@@ -204,7 +204,9 @@ size_t moe_route_dispatch_workspace_bytes(int64_t n_tokens, int32_t n_experts, i
  *   by the dispatch), topk_w [N, k] f32 (output); every other argument as in
  *   moe_dispatch; workspace of moe_route_dispatch_workspace_bytes(N, E, k, G).
  * In the identity layout (unsorted, G == 1) row t*k+j is x[t] whatever the
- * routing chooses, so the routing and the row copy run in one launch.
+ * routing chooses, so the routing and the row copy run in one launch; other
+ * layouts take moe_dispatch's launches after the routing launch (with its
+ * shared positions + row copy launch, bounded wait and validate-mode report).
  * Errors: those of moe_route_topk and moe_dispatch. */
 int moe_route_dispatch(const float* logits, int32_t renormalize, int32_t* topk_idx, float* topk_w,
                        const void* x, const float* x_scales, int32_t dtype, int64_t n_tokens,
@@ -229,7 +231,8 @@ int moe_route_dispatch(const float* logits, int32_t renormalize, int32_t* topk_i
  * routine) and needs no zeroed memory: every scratch byte it reads was
  * written earlier in the same call.  All calls on one GPU share the array, so
  * calls that overlap on one GPU (other streams, other host threads) race:
- * serialise them.
+ * serialise them.  Validate mode does not apply (it would copy to the host
+ * and wait).
  * Errors: those of moe_route_dispatch; MOE_ERR_UNSUPPORTED when
  * moe_route_dispatch_workspace_bytes(N, E, k, G) exceeds
  * MOE_NOALLOC_SCRATCH_BYTES (E <= 256 always fits; E = 1024 fits up to

@@ -1,5 +1,7 @@
 """moe_route_dispatch equals moe_route_topk followed by moe_dispatch, bit for
 bit, and both equal the oracle."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -109,3 +111,83 @@ def test_fp8_segment_workload_and_auto_mode():
     for sort in (0, 1, -1):
         _compare(inp["logits"], inp["x"], cfg.top_k, cfg.n_segments, sort, x_scales=inp["x_scales"],
                  cutoff=512)
+
+
+@pytest.mark.parametrize("n,e,k,g,sort,dtype,d", [
+    (4096, 256, 8, 1, 1, "bf16", 7168),    # prefill shape
+    (8192, 8, 2, 1, 1, "bf16", 4096),      # Mixtral-like shape
+    (1024, 256, 8, 8, 0, "f8", 7168),      # segment-major fp8 rows and block scales
+    (3001, 256, 8, 4, 1, "f32", 100),      # ragged last chunk, 400-byte rows
+    (2100, 100, 9, 10, 0, "bf16", 8),      # one 16-byte vector per row
+    (4097, 584, 1, 1, 1, "bf16", 64),      # the largest E whose rank LDS fits 16 KB
+])
+def test_rank_and_copy_launch_in_validate_mode(n, e, k, g, sort, dtype, d):
+    """moe_route_dispatch where positions and row copy share a launch (16-byte
+    rows, above 4096 pairs, outside the identity layout, rank LDS within 16
+    KB), with validate mode on: the call waits and fails if any copy wave
+    gave up waiting for its positions; every map and row is compared with the
+    oracle's routing and dispatch."""
+    rng = np.random.default_rng(n + e + d)
+    logits = rng.standard_normal((n, e)).astype(np.float32)
+    xs = None
+    if dtype == "f8":
+        x = rng.integers(0, 256, (n, d), dtype=np.uint8)
+        x[(x & 0x7F) == 0x7F] = 0
+        xs = rng.uniform(0.5, 2.0, (n, d // 128)).astype(np.float32)
+    elif dtype == "bf16":
+        x = rng.integers(0, 2**16, (n, d), dtype=np.uint16)
+    else:
+        x = rng.standard_normal((n, d)).astype(np.float32)
+    os.environ["MOE_DC_VALIDATE"] = "1"
+    try:
+        idx, _, res = moe.moe_route_dispatch(to_dev(logits), to_dev(x), k, g, True, sort,
+                                             x_scales=None if xs is None else to_dev(xs))
+    finally:
+        del os.environ["MOE_DC_VALIDATE"]
+    oi, _ = oracle_route(logits, k, True)
+    assert np.array_equal(to_np(idx), oi)
+    ref = od.dispatch(oi, e, g, bool(sort), x=x, x_scales=xs)
+    for name in MAPS:
+        assert np.array_equal(to_np(getattr(res, name)), ref[name]), name
+    assert np.array_equal(to_np(res.rows).view(np.uint8), ref["rows"].view(np.uint8))
+    if xs is not None:
+        assert np.array_equal(to_np(res.row_scales), ref["row_scales"])
+
+
+def test_rank_and_copy_give_up_path_is_reported():
+    """moe_route_dispatch's shared rank + copy launch: with the copy waves'
+    poll limit forced to 0 from the host (MOE_DC_SPIN_LIMIT, a test hook),
+    waves that find their positions not yet published give up at once, the
+    launch still ends normally, those rows are skipped and validate mode
+    reports it (at the prefill size this is all but certain; a call where no
+    wave had to wait must then be exact).  The next call, with the default
+    limit, is exact."""
+    cfg = CONFIGS["prefill"]
+    inp = make_inputs(cfg)
+    logits = to_dev(inp["logits"])
+    x = to_dev(inp["x"])
+    oi, _ = oracle_route(inp["logits"], cfg.top_k, cfg.renormalize)
+    ref = od.dispatch(oi, cfg.n_experts, 1, True)
+    rng = np.random.default_rng(5)
+    sample = rng.integers(0, cfg.n_tokens * cfg.top_k, 4000)
+
+    def exact(res):
+        for name in MAPS:
+            assert np.array_equal(to_np(getattr(res, name)), ref[name]), name
+        rows = res.rows[torch.from_numpy(sample).to(DEV)]
+        assert np.array_equal(to_np(rows), inp["x"][ref["src_pair"][sample] // cfg.top_k])
+
+    os.environ["MOE_DC_VALIDATE"] = "1"
+    try:
+        os.environ["MOE_DC_SPIN_LIMIT"] = "0"
+        try:
+            _, _, res = moe.moe_route_dispatch(logits, x, cfg.top_k, 1, cfg.renormalize, 1)
+            exact(res)
+        except moe.MoeError as err:
+            assert "gave up" in str(err)
+        finally:
+            del os.environ["MOE_DC_SPIN_LIMIT"]
+        _, _, res = moe.moe_route_dispatch(logits, x, cfg.top_k, 1, cfg.renormalize, 1)
+        exact(res)
+    finally:
+        del os.environ["MOE_DC_VALIDATE"]
