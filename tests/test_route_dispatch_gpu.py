@@ -120,13 +120,18 @@ def test_fp8_segment_workload_and_auto_mode():
     (3001, 256, 8, 4, 1, "f32", 100),      # ragged last chunk, 400-byte rows
     (2100, 100, 9, 10, 0, "bf16", 8),      # one 16-byte vector per row
     (4097, 584, 1, 1, 1, "bf16", 64),      # the largest E whose rank LDS fits 16 KB
+    (4097, 585, 1, 1, 1, "bf16", 64),      # one expert more: ranks and copy in separate launches
+    (128, 256, 8, 1, 0, "bf16", 7168),     # identity layout: routing and row copy in one launch
+    (300, 64, 4, 2, 1, "bf16", 64),        # 1200 pairs: the one-workgroup metadata path
 ])
-def test_rank_and_copy_launch_in_validate_mode(n, e, k, g, sort, dtype, d):
-    """moe_route_dispatch where positions and row copy share a launch (16-byte
-    rows, above 4096 pairs, outside the identity layout, rank LDS within 16
-    KB), with validate mode on: the call waits and fails if any copy wave
-    gave up waiting for its positions; every map and row is compared with the
-    oracle's routing and dispatch."""
+def test_route_dispatch_in_validate_mode(n, e, k, g, sort, dtype, d):
+    """moe_route_dispatch with validate mode on, over its launch forms: positions
+    and row copy in one launch (16-byte rows, above 4096 pairs, outside the
+    identity layout, rank LDS within 16 KB), in separate launches (E = 585),
+    the identity layout's routing-and-copy launch and the one-workgroup
+    metadata path.  The call waits and fails if any copy wave gave up waiting
+    for its positions; every map and row is compared with the oracle's
+    routing and dispatch."""
     rng = np.random.default_rng(n + e + d)
     logits = rng.standard_normal((n, e)).astype(np.float32)
     xs = None
